@@ -1,0 +1,183 @@
+"""Benchmark: MXFP4 Wgrad including the Hadamard rotation and quantization of
+both operands, on the Llama-3.1-8B MLP gate/up layer (T = 8192 tokens,
+N = 14336 out-features, K = 4096 in-features), on one MI355X.
+
+A step is the whole hot path over one batch: rotate (deterministic
+Hadamard-32 along tokens) and quantize dY[T, N] and X[T, K] to MXFP4 (RTN),
+then dW[N, K] = dY^T X on the scaled FP4 matrix cores, fp32 output.  Inputs
+are synthetic bf16 tensors resident in HBM before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload gate_up] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
+(2 T N K flops over the whole step); the roofline object describes the
+dominant kernel (the GEMM) from per-launch HIP events; cpu_baseline times
+the plain CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MXFP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "MXFP4 Wgrad TFLOPS incl. Hadamard+quantize (8192×14336×4096); quantizer GB/s"
+COUNTERS = os.path.join(ROOT, "profiles", "gemm_mx_wgrad_gate_up_counters.json")
+GEMM_SRC = os.path.join(ROOT, "fp4_precision_gemms_amd", "csrc", "gemm_mx.hip")
+
+
+def quant_bytes(elems: int) -> float:
+    """Algorithmic bytes of one MXFP4 quantization: 2 B bf16 read, 0.5 B of
+    codes and 1/32 B of scale written per element."""
+    return elems * (2.0 + 0.5 + 1.0 / 32.0)
+
+
+def traffic_per_launch():
+    """HBM bytes per GEMM launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+        src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+        if rec.get("gemm_source_sha256") == src:
+            return float(rec["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def cpu_baseline(w, dY, X):
+    """The oracle, untuned, on a bounded sample of the same Wgrad: the
+    rotation + quantization of 8192 of dY's 14336 token-columns and of all of
+    X, and 8192 of dW's rows in binary64; each part scaled to the full layer
+    by its row count.  Returns the JSON object."""
+    import oracle as O
+
+    n = 8192
+    t0 = time.perf_counter()
+    aq, as_ = O.quant_mx(dY, O.AXIS_ROWS, 32, O.HAD_DET, 0, O.RND_RTN, 0, r0=0, r1=n)
+    t1 = time.perf_counter()
+    bq, bs = O.quant_mx(X, O.AXIS_ROWS, 32, O.HAD_DET)
+    t2 = time.perf_counter()
+    O.gemm_rows(aq, as_, bq, bs, 0, n)
+    t3 = time.perf_counter()
+    t_full = (t1 - t0) * w.N / n + (t2 - t1) + (t3 - t2) * w.N / n
+    flops = 2.0 * w.T * w.N * w.K
+    return {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": "Hadamard-32 + MXFP4 quantization of %d of %d dY token-columns and of all "
+                      "%d X columns, then %d of %d dW rows by the binary64 oracle GEMM; "
+                      "measured %.1f s, scaled per part to the full layer (%.0f s)"
+                      % (n, w.N, w.K, n, w.N, t3 - t0, t_full)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gate_up")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp4_precision_gemms_amd as F
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    F.lib()
+    w = W.WORKLOADS[args.workload]
+    T, N, K = w.T, w.N, w.K
+    dev = torch.device("cuda:0")
+    dY_np, X_np = W.tensor(w, "dY"), W.tensor(w, "X")
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    dY, X = up(dY_np), up(X_np)
+    dytq = torch.empty((N, T // 2), dtype=torch.uint8, device=dev)
+    dyts = torch.empty((N, T // 32), dtype=torch.uint8, device=dev)
+    xtq = torch.empty((K, T // 2), dtype=torch.uint8, device=dev)
+    xts = torch.empty((K, T // 32), dtype=torch.uint8, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        F.fp4_hadamard_quantize(dY, F.AXIS_ROWS, 32, F.HAD_DET, 0, F.RTN, 0, dytq, dyts)
+        if ev is not None:
+            ev[1].record(stream)
+        F.fp4_hadamard_quantize(X, F.AXIS_ROWS, 32, F.HAD_DET, 0, F.RTN, 0, xtq, xts)
+        if ev is not None:
+            ev[2].record(stream)
+        F.fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=dw)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
+
+    t_qdy, t_qx, t_gemm = avg(0, 1), avg(1, 2), avg(2, 3)
+    flops = 2.0 * T * N * K
+    gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
+    q_gbs = (quant_bytes(T * N) + quant_bytes(T * K)) / ((t_qdy + t_qx) * 1e-3) / 1e9
+    traffic = traffic_per_launch()
+    out = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "%s Wgrad incl. Hadamard-32 + MXFP4 quantize" % w.name,
+                   "T": T, "N": N, "K": K, "hadamard": "deterministic-32 along tokens",
+                   "rounding": "rtn", "output": "fp32 dW[N,K]"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_mx_tn (Wgrad)",
+                     "achieved": gemm_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / MXFP4_PEAK_TFLOPS, "traffic": traffic},
+        "breakdown": {"quant_dY_ms": t_qdy, "quant_X_ms": t_qx, "gemm_ms": t_gemm,
+                      "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
+                      "gemm_TFLOPs": gemm_tflops},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, dY_np, X_np)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,181 @@
+"""Python binding of libfp4.so, the MXFP4 / NVFP4 block-quantized linear layer
+for AMD Instinct MI355X (gfx950).
+
+The functions below carry the names of the C entry points (include/fp4.h)
+and only marshal arguments: shapes and pointers of torch tensors in, status
+codes out.  Every step of the computation runs in the HIP kernels of the
+library.  torch supplies device memory and the current HIP stream.
+
+If libfp4.so has not been built (``python -m fp4_precision_gemms_amd.build``)
+every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+AXIS_COLS, AXIS_ROWS = 0, 1
+HAD_NONE, HAD_DET, HAD_SIGNED = 0, 1, 2
+RTN, SR = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4.so")
+_lib = None
+
+
+class Fp4Error(RuntimeError):
+    """A nonzero fp4_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp4.so with argument types set; raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfp4.so is not built: run `python -m fp4_precision_gemms_amd.build` "
+                           "(expected at %s)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, u64, i32, vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
+    L.fp4_hadamard_quantize.argtypes = [vp, i64, i64, i32, i32, i32, u64, i32, u64, vp, vp, vp]
+    L.fp4_hadamard_quantize.restype = i32
+    for name in ("fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        fn.restype = i32
+    L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, u64, i32, u64, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_workspace_bytes.argtypes = [i64, i64]
+    L.nvfp4_workspace_bytes.restype = ctypes.c_size_t
+    L.fp4_status_string.argtypes = [i32]
+    L.fp4_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def fp4_status_string(status: int) -> str:
+    return lib().fp4_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise Fp4Error(status, fp4_status_string(status))
+
+
+def _stream_ptr(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def mx_shapes(rows: int, cols: int, axis: int):
+    """(codes shape, scales shape) of fp4_hadamard_quantize's outputs."""
+    R, C = (rows, cols) if axis == AXIS_COLS else (cols, rows)
+    return (R, C // 2), (R, C // 32)
+
+
+def fp4_hadamard_quantize(x: torch.Tensor, axis: int = AXIS_COLS, had_n: int = 32,
+                          had: int = HAD_NONE, sign_seed: int = 0, rnd: int = RTN,
+                          sr_seed: int = 0, codes: torch.Tensor | None = None,
+                          scales: torch.Tensor | None = None, stream=None):
+    """MXFP4 codes and E8M0 scales of bf16 x[rows, cols] (see include/fp4.h)."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    cshape, sshape = mx_shapes(rows, cols, axis)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if tuple(codes.shape) != cshape or tuple(scales.shape) != sshape:
+        raise ValueError("output shapes must be %s and %s" % (cshape, sshape))
+    _check(lib().fp4_hadamard_quantize(x.data_ptr(), rows, cols, axis, had_n, had,
+                                       sign_seed & (2 ** 64 - 1), rnd, sr_seed & (2 ** 64 - 1),
+                                       codes.data_ptr(), scales.data_ptr(),
+                                       _stream_ptr(stream, x.device)))
+    return codes, scales
+
+
+def _gemm(fn, aq, as_, bq, bs, T, N, K, out_shape, out, stream):
+    for t, n in ((aq, "a codes"), (as_, "a scales"), (bq, "b codes"), (bs, "b scales")):
+        _need(t, torch.uint8, n)
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.float32, device=aq.device)
+    _need(out, torch.float32, "out")
+    if tuple(out.shape) != tuple(out_shape):
+        raise ValueError("out must have shape %s" % (out_shape,))
+    _check(fn(aq.data_ptr(), as_.data_ptr(), bq.data_ptr(), bs.data_ptr(), T, N, K,
+              out.data_ptr(), _stream_ptr(stream, aq.device)))
+    return out
+
+
+def fp4_gemm_fprop(xq, xs, wq, ws, out=None, stream=None):
+    """y[T, N] = X W^T from xq [T, K/2] and wq [N, K/2] (both blocked along K)."""
+    T, K, N = xq.shape[0], xq.shape[1] * 2, wq.shape[0]
+    if wq.shape[1] * 2 != K or xs.shape != (T, K // 32) or ws.shape != (N, K // 32):
+        raise ValueError("fprop operand shapes disagree")
+    return _gemm(lib().fp4_gemm_fprop, xq, xs, wq, ws, T, N, K, (T, N), out, stream)
+
+
+def fp4_gemm_dgrad(dyq, dys, wtq, wts, out=None, stream=None):
+    """dx[T, K] = dY W from dyq [T, N/2] (blocked along N) and wtq [K, N/2]."""
+    T, N, K = dyq.shape[0], dyq.shape[1] * 2, wtq.shape[0]
+    if wtq.shape[1] * 2 != N or dys.shape != (T, N // 32) or wts.shape != (K, N // 32):
+        raise ValueError("dgrad operand shapes disagree")
+    return _gemm(lib().fp4_gemm_dgrad, dyq, dys, wtq, wts, T, N, K, (T, K), out, stream)
+
+
+def fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=None, stream=None):
+    """dw[N, K] = dY^T X from dytq [N, T/2] and xtq [K, T/2] (blocked along T)."""
+    N, T, K = dytq.shape[0], dytq.shape[1] * 2, xtq.shape[0]
+    if xtq.shape[1] * 2 != T or dyts.shape != (N, T // 32) or xts.shape != (K, T // 32):
+        raise ValueError("wgrad operand shapes disagree")
+    return _gemm(lib().fp4_gemm_wgrad, dytq, dyts, xtq, xts, T, N, K, (N, K), out, stream)
+
+
+def nvfp4_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().nvfp4_workspace_bytes(rows, cols))
+
+
+def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, renorm: int = 1,
+                   sr_seed: int = 0, amax_in: torch.Tensor | None = None,
+                   codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                   tensor_scale: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None):
+    """NVFP4 codes [rows, cols/2], E4M3 scales [rows, cols/16] and the fp32
+    tensor scale (a 1-element device tensor) of bf16 x (see include/fp4.h)."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    dev = x.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev) if scales is None else scales
+    tensor_scale = torch.empty(1, dtype=torch.float32, device=dev) if tensor_scale is None else tensor_scale
+    if amax_in is None and workspace is None:
+        workspace = torch.empty(nvfp4_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    _check(lib().nvfp4_quantize(x.data_ptr(), rows, cols, had, sign_seed & (2 ** 64 - 1), renorm,
+                                sr_seed & (2 ** 64 - 1), _ptr(amax_in), codes.data_ptr(),
+                                scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),
+                                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream_ptr(stream, dev)))
+    return codes, scales, tensor_scale

@@ -1,0 +1,120 @@
+// fp4_abi.cpp -- the C ABI of libfp4.so (declared in include/fp4.h):
+// argument validation, then dispatch to the HIP launchers.  No HIP call is
+// made before every argument has been checked, so error paths can be
+// exercised on machines without a GPU.
+#include "fp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "fp4_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// a * b stays far from int64 overflow (byte counts of bf16 / fp32 tensors)
+bool product_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= (INT64_C(1) << 60) / b; }
+
+fp4_status from_hip(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_LAUNCH; }
+
+fp4_status check_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                      const float* c, int64_t M, int64_t N, int64_t K) {
+    if (!aq || !as || !bq || !bs || !c) return FP4_ERR_NULL;
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32) return FP4_ERR_SHAPE;
+    if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N) || M > INT32_MAX ||
+        N > INT32_MAX)
+        return FP4_ERR_SHAPE;
+    if (!aligned16(aq) || !aligned16(as) || !aligned16(bq) || !aligned16(bs) || !aligned16(c))
+        return FP4_ERR_ALIGN;
+    return FP4_OK;
+}
+
+fp4_status run_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                    int64_t M, int64_t N, int64_t K, float* c, void* stream) {
+    const fp4_status s = check_gemm(aq, as, bq, bs, c, M, N, K);
+    if (s != FP4_OK) return s;
+    return from_hip(fp4dev::launch_gemm_mx(aq, as, bq, bs, M, N, K, c, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status fp4_hadamard_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_axis axis,
+                                 int had_n, fp4_hadamard had, uint64_t sign_seed, fp4_rounding rnd,
+                                 uint64_t sr_seed, uint8_t* codes, uint8_t* scales_e8m0,
+                                 void* stream) {
+    if (axis != FP4_AXIS_COLS && axis != FP4_AXIS_ROWS) return FP4_ERR_ENUM;
+    if (had != FP4_HAD_NONE && had != FP4_HAD_DET && had != FP4_HAD_SIGNED) return FP4_ERR_ENUM;
+    if (had != FP4_HAD_NONE && had_n != 16 && had_n != 32) return FP4_ERR_ENUM;
+    if (rnd != FP4_RTN && rnd != FP4_SR) return FP4_ERR_ENUM;
+    if (!x_bf16 || !codes || !scales_e8m0) return FP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || !product_ok(rows, cols)) return FP4_ERR_SHAPE;
+    const int64_t contraction = axis == FP4_AXIS_COLS ? cols : rows;
+    if (contraction % 32) return FP4_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales_e8m0)) return FP4_ERR_ALIGN;
+    return from_hip(fp4dev::launch_quant_mx(x_bf16, rows, cols, (int)axis, had_n, (int)had,
+                                            sign_seed, (int)rnd, sr_seed, codes, scales_e8m0,
+                                            (hipStream_t)stream));
+}
+
+fp4_status fp4_gemm_fprop(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, int64_t T, int64_t N, int64_t K, float* y,
+                          void* stream) {
+    return run_gemm(xq, xs, wq, ws, T, N, K, y, stream);        // [T,K] x [N,K]^T
+}
+
+fp4_status fp4_gemm_dgrad(const uint8_t* dyq, const uint8_t* dys, const uint8_t* wtq,
+                          const uint8_t* wts, int64_t T, int64_t N, int64_t K, float* dx,
+                          void* stream) {
+    return run_gemm(dyq, dys, wtq, wts, T, K, N, dx, stream);   // [T,N] x [K,N]^T
+}
+
+fp4_status fp4_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, const uint8_t* xtq,
+                          const uint8_t* xts, int64_t T, int64_t N, int64_t K, float* dw,
+                          void* stream) {
+    return run_gemm(dytq, dyts, xtq, xts, N, K, T, dw, stream);  // [N,T] x [K,T]^T
+}
+
+size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols) {
+    (void)rows;
+    (void)cols;
+    return 256;   // one 32-bit amax word, padded to the allocation granule
+}
+
+fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
+                          uint64_t sign_seed, int renorm, uint64_t sr_seed, const float* amax_in,
+                          uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (had != FP4_HAD_NONE && had != FP4_HAD_DET && had != FP4_HAD_SIGNED) return FP4_ERR_ENUM;
+    if (renorm != 0 && renorm != 1) return FP4_ERR_ENUM;
+    if (!x_bf16 || !codes || !scales_e4m3 || !tensor_scale) return FP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || cols % 16 || !product_ok(rows, cols)) return FP4_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales_e4m3) ||
+        !aligned4(tensor_scale) || (amax_in && !aligned4(amax_in)))
+        return FP4_ERR_ALIGN;
+    if (!amax_in) {
+        if (!workspace || workspace_bytes < nvfp4_workspace_bytes(rows, cols))
+            return FP4_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FP4_ERR_ALIGN;
+    }
+    return from_hip(fp4dev::launch_nvfp4(x_bf16, rows, cols, (int)had, sign_seed, renorm, sr_seed,
+                                         amax_in, codes, scales_e4m3, tensor_scale, workspace,
+                                         (hipStream_t)stream));
+}
+
+const char* fp4_status_string(fp4_status status) {
+    switch (status) {
+        case FP4_OK: return "FP4_OK";
+        case FP4_ERR_NULL: return "FP4_ERR_NULL: a required pointer is NULL";
+        case FP4_ERR_SHAPE: return "FP4_ERR_SHAPE: bad size or contraction not a multiple of the block";
+        case FP4_ERR_ALIGN: return "FP4_ERR_ALIGN: pointer not 16-byte aligned";
+        case FP4_ERR_ENUM: return "FP4_ERR_ENUM: unknown axis, Hadamard mode/size or rounding";
+        case FP4_ERR_LAUNCH: return "FP4_ERR_LAUNCH: HIP kernel launch failed";
+        case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE: workspace missing or too small";
+    }
+    return "FP4_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// fp4_launch.hpp -- internal launchers behind the C ABI (validated arguments
+// only; every pointer and size has been checked by the caller).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+// MXFP4 quantization of bf16 x[rows, cols] along axis 0 (cols) or 1 (rows).
+hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, int had_n, int had,
+                           uint64_t sign_seed, int rnd, uint64_t sr_seed, uint8_t* codes,
+                           uint8_t* scales, hipStream_t st);
+
+// C[M, N] (fp32, row-major) = A[M, K] B[N, K]^T over MXFP4 operands.
+hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
+                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
+                          hipStream_t st);
+
+// NVFP4 quantization; amax_dev is either the caller's amax_in or the
+// workspace the amax pass writes.
+hipError_t launch_nvfp4(const void* x, int64_t rows, int64_t cols, int had, uint64_t sign_seed,
+                        int renorm, uint64_t sr_seed, const float* amax_in, uint8_t* codes,
+                        uint8_t* scales, float* tensor_scale, void* workspace, hipStream_t st);
+
+uint32_t host_sign_word(int had, uint64_t seed);
+
+}  // namespace fp4dev

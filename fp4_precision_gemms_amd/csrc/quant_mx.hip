@@ -1,0 +1,293 @@
+// quant_mx.hip -- Hadamard rotation + MXFP4 quantization kernels for gfx950.
+//
+// Block format: [AMD-MXFP4] "Pretraining large language models with MXFP4 on
+// Native FP4 Hardware", section "Что такое MXFP4": 32-element blocks sharing
+// one E8M0 exponent, E2M1 elements rounded to the nearest value.  Rotation:
+// same page, section "Поисковая экспериментальная работа: корень
+// нестабильности": a Hadamard transform, deterministic or after random sign
+// flips, applied before quantization.
+//
+// Two kernels, one per block axis:
+//   quant_mx_along_cols -- blocks run along the contiguous dim.  A lane owns 8
+//     consecutive elements (one 16-byte load); four adjacent lanes own a
+//     block.  The first three butterfly stages are in registers, the strides
+//     8 and 16 cross lanes through DPP quad permutes, the block maximum is a
+//     two-step DPP reduction, and each lane stores its 8 codes as one dword.
+//   quant_mx_along_rows -- blocks run along the strided dim (x^T is
+//     quantized, as Wgrad needs: blocks along tokens).  A lane owns CPL
+//     adjacent columns and a 32-row block of each: it issues 32 row loads
+//     (adjacent lanes read adjacent columns, so every load instruction reads
+//     one contiguous 64*CPL*2-byte row segment), then transforms, reduces and
+//     encodes each column entirely in registers and stores 16 code bytes.
+#include "fp4_device.hpp"
+#include "fp4_launch.hpp"
+
+namespace fp4dev {
+namespace {
+
+// Quad permutes: partner lane q^1 and q^2 inside each group of four lanes.
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+}
+__device__ __forceinline__ float quad_xor1f(float v) { return __uint_as_float(quad_xor1(__float_as_uint(v))); }
+__device__ __forceinline__ float quad_xor2f(float v) { return __uint_as_float(quad_xor2(__float_as_uint(v))); }
+
+// In-register butterflies with strides 1, 2, 4 over a[0..7].
+__device__ __forceinline__ void butterfly8(float* a) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & h) continue;
+            const float x = a[i], y = a[i + h];
+            a[i] = x + y;
+            a[i + h] = x - y;
+        }
+    }
+}
+
+// Encodes 8 rotated values of one lane into 8 nibbles (element 0 lowest).
+template <bool SR>
+__device__ __forceinline__ uint32_t encode8(const float* y, float inv, uint4 u0, uint4 u1) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float v = y[t] * inv;
+        uint32_t c;
+        if constexpr (SR) c = e2m1_sr(v, word_of(t < 4 ? u0 : u1, t & 3));
+        else c = e2m1_rtn(v);
+        w |= c << (4 * t);
+    }
+    return w;
+}
+
+constexpr int kColsThreads = 256;
+constexpr int kColsUnroll = 4;
+
+// HADN: 0 (no rotation), 16 or 32.
+template <int HADN, bool SR>
+__global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
+    const uint4* __restrict__ x, int64_t nchunks, uint32_t sign_word, float norm,
+    uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint4 w[kColsUnroll];
+    int64_t g[kColsUnroll];
+#pragma unroll
+    for (int u = 0; u < kColsUnroll; ++u) {
+        g[u] = ((int64_t)blockIdx.x * kColsUnroll + u) * kColsThreads + threadIdx.x;
+        if (g[u] < nchunks) w[u] = x[g[u]];
+    }
+    const int q = threadIdx.x & 3;                 // lane within the block of 4
+#pragma unroll
+    for (int u = 0; u < kColsUnroll; ++u) {
+        if (g[u] >= nchunks) break;                // uniform per quad: nchunks % 4 == 0
+        float a[8] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y),
+                      bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
+        if constexpr (HADN != 0) {
+            const int sbase = (8 * q) % HADN;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) a[t] = flip_if(a[t], (sign_word >> (sbase + t)) & 1u);
+            butterfly8(a);
+            // stride 8: pair (i, i+8) lives in lanes (q, q^1); the lower lane adds
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float p = quad_xor1f(a[t]);
+                a[t] = (q & 1) ? (p - a[t]) : (a[t] + p);
+            }
+            if constexpr (HADN == 32) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float p = quad_xor2f(a[t]);
+                    a[t] = (q & 2) ? (p - a[t]) : (a[t] + p);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) a[t] = a[t] * norm;
+        }
+        // block maximum of |y| as unsigned bits (NaN > Inf > finite)
+        uint32_t m = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(a[t]) & 0x7FFFFFFFu);
+        m = max(m, quad_xor1(m));
+        m = max(m, quad_xor2(m));
+        const uint32_t byte = e8m0_from_amax_bits(m);
+        uint32_t word = 0;
+        if (byte != 255u) {
+            uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+            if constexpr (SR) {
+                u0 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2);
+                u1 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2 + 1);
+            }
+            word = encode8<SR>(a, inv_scale_from_e8m0(byte), u0, u1);
+        }
+        codes[g[u]] = word;
+        if (q == 0) scales[g[u] >> 2] = (uint8_t)byte;
+    }
+}
+
+template <int CPL> struct ColVec;
+template <> struct ColVec<1> { using T = uint16_t; };
+template <> struct ColVec<2> { using T = uint32_t; };
+template <> struct ColVec<4> { using T = uint2; };
+
+template <int CPL>
+__device__ __forceinline__ float col_value(const typename ColVec<CPL>::T& v, int c) {
+    if constexpr (CPL == 1) return __uint_as_float((uint32_t)v << 16);
+    else if constexpr (CPL == 2) return c == 0 ? bf16_lo(v) : bf16_hi(v);
+    else {
+        const uint32_t w = c < 2 ? v.x : v.y;
+        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
+constexpr int kRowsWaves = 4;
+
+// One lane: CPL columns x RBW consecutive 32-row blocks.
+template <int CPL, int HADN, bool SR, int RBW>
+__global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
+    uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    using V = typename ColVec<CPL>::T;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * CPL;
+    if (col0 >= cols) return;                      // no cross-lane work in this kernel
+    const int64_t nrb = rows / 32;
+    const int64_t rb0 = ((int64_t)blockIdx.y * kRowsWaves + wave) * RBW;
+    for (int i = 0; i < RBW; ++i) {
+        const int64_t rb = rb0 + i;
+        if (rb >= nrb) break;
+        V v[32];
+        const V* src = reinterpret_cast<const V*>(x + rb * 32 * cols + col0);
+        const int64_t vstride = cols / CPL;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) v[r] = src[r * vstride];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float a[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) a[r] = col_value<CPL>(v[r], c);
+            if constexpr (HADN != 0) {
+#pragma unroll
+                for (int r = 0; r < 32; ++r) a[r] = flip_if(a[r], (sign_word >> (r % HADN)) & 1u);
+#pragma unroll
+                for (int h = 1; h < HADN; h <<= 1) {
+#pragma unroll
+                    for (int r = 0; r < 32; ++r) {
+                        if (r & h) continue;
+                        const float p = a[r], s = a[r + h];
+                        a[r] = p + s;
+                        a[r + h] = p - s;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 32; ++r) a[r] = a[r] * norm;
+            }
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) m = max(m, __float_as_uint(a[r]) & 0x7FFFFFFFu);
+            const uint32_t byte = e8m0_from_amax_bits(m);
+            const int64_t col = col0 + c;
+            uint4 out = make_uint4(0, 0, 0, 0);
+            if (byte != 255u) {
+                const float inv = inv_scale_from_e8m0(byte);
+                const uint64_t gbase = ((uint64_t)col * (uint64_t)rows + (uint64_t)rb * 32) >> 2;
+                uint32_t wd[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+                    if constexpr (SR) {
+                        u0 = stream4(sr_seed, 0u, gbase + 2 * k);
+                        u1 = stream4(sr_seed, 0u, gbase + 2 * k + 1);
+                    }
+                    wd[k] = encode8<SR>(a + 8 * k, inv, u0, u1);
+                }
+                out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+            *reinterpret_cast<uint4*>(codes + col * (rows / 2) + rb * 16) = out;
+            scales[col * (rows / 32) + rb] = (uint8_t)byte;
+        }
+    }
+}
+
+template <int HADN, bool SR>
+hipError_t launch_cols(const void* x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
+                       uint64_t sr_seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+    const int64_t nchunks = rows * cols / 8;
+    const int64_t per_block = (int64_t)kColsThreads * kColsUnroll;
+    const int64_t blocks = (nchunks + per_block - 1) / per_block;
+    hipLaunchKernelGGL((quant_mx_along_cols<HADN, SR>), dim3((unsigned)blocks), dim3(kColsThreads),
+                       0, st, (const uint4*)x, nchunks, sign_word, norm, sr_seed,
+                       (uint32_t*)codes, scales);
+    return hipGetLastError();
+}
+
+template <int CPL, int HADN, bool SR>
+hipError_t launch_rows(const void* x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
+                       uint64_t sr_seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+    constexpr int RBW = 4;
+    const int64_t nrb = rows / 32;
+    const int64_t gx = (cols + 64 * CPL - 1) / (64 * CPL);
+    const int64_t gy = (nrb + kRowsWaves * RBW - 1) / (kRowsWaves * RBW);
+    hipLaunchKernelGGL((quant_mx_along_rows<CPL, HADN, SR, RBW>), dim3((unsigned)gx, (unsigned)gy),
+                       dim3(64 * kRowsWaves), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
+                       sr_seed, codes, scales);
+    return hipGetLastError();
+}
+
+template <int HADN, bool SR>
+hipError_t dispatch_rows_cpl(const void* x, int64_t rows, int64_t cols, uint32_t sign_word,
+                             float norm, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
+                             hipStream_t st) {
+    if (cols % 4 == 0) return launch_rows<4, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
+    if (cols % 2 == 0) return launch_rows<2, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
+    return launch_rows<1, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
+}
+
+template <int HADN>
+hipError_t dispatch_rnd(int axis, bool sr, const void* x, int64_t rows, int64_t cols,
+                        uint32_t sign_word, float norm, uint64_t sr_seed, uint8_t* codes,
+                        uint8_t* scales, hipStream_t st) {
+    if (axis == 0) {
+        return sr ? launch_cols<HADN, true>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st)
+                  : launch_cols<HADN, false>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
+    }
+    return sr ? dispatch_rows_cpl<HADN, true>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st)
+              : dispatch_rows_cpl<HADN, false>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
+}
+
+}  // namespace
+
+// Host-side sign word of the randomized transform: bit j of word 0 of the
+// purpose-1 Philox stream (host copy of the device generator, same rounds).
+uint32_t host_sign_word(int had, uint64_t seed) {
+    if (had != 2) return 0u;
+    uint32_t c[4] = {0u, 0u, 1u, 0u};
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0, n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1, n3 = (uint32_t)p0;
+        c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+    }
+    return c[0];
+}
+
+hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, int had_n, int had,
+                           uint64_t sign_seed, int rnd, uint64_t sr_seed, uint8_t* codes,
+                           uint8_t* scales, hipStream_t st) {
+    const uint32_t sw = host_sign_word(had, sign_seed);
+    const bool sr = rnd == 1;
+    if (had == 0) return dispatch_rnd<0>(axis, sr, x, rows, cols, 0u, 1.0f, sr_seed, codes, scales, st);
+    if (had_n == 16) {
+        return dispatch_rnd<16>(axis, sr, x, rows, cols, sw, 0.25f, sr_seed, codes, scales, st);
+    }
+    // fl(1/sqrt(32)) = 0x3E3504F3
+    return dispatch_rnd<32>(axis, sr, x, rows, cols, sw, __builtin_bit_cast(float, 0x3E3504F3u),
+                            sr_seed, codes, scales, st);
+}
+
+}  // namespace fp4dev

@@ -1,0 +1,190 @@
+/*
+ * fp4.h -- C ABI of libfp4.so: the block-quantized linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer is three GEMMs (Fprop Y = X W^T, Dgrad dX = dY W, Wgrad
+ * dW = dY^T X), each run on MXFP4 operands: blocks of 32 elements that share
+ * one E8M0 power-of-two exponent, each element an E2M1 4-bit float.  Before
+ * quantization an operand may be rotated block-wise by a Hadamard transform,
+ * plain (the same every step) or after seeded random sign flips.  A second
+ * quantizer produces NVFP4 (16-element blocks, E4M3 block scales, an fp32
+ * tensor scale) with a renormalization folded into the block scales by
+ * stochastic rounding.
+ *
+ * Pages this interface follows (title, then section):
+ *   [AMD-MXFP4]  "Pretraining large language models with MXFP4 on Native FP4
+ *                Hardware" (htx.com news item): "Что такое MXFP4" (the block
+ *                format), "Поисковая экспериментальная работа: корень
+ *                нестабильности" (the three GEMMs; stochastic rounding;
+ *                randomized vs deterministic Hadamard), and the figure caption
+ *                of section "Сквозная эффективность" (the transform "H16").
+ *   [QUARTET-II] "Quartet II -- обучение в NVFP4 с точными несмещёнными
+ *                градиентами" (Telegram post): NVFP4 with FP8 scales,
+ *                renormalization folded into the scales by stochastic rounding.
+ *   [NV-NVFP4]   "NVIDIA создала метод обучения нейросетей в 4-bit точности":
+ *                "Как это работает" (16x16 random Hadamard transforms).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers (hipMalloc / torch CUDA tensors) owned by
+ *     the caller, 16-byte aligned, tensors contiguous row-major.  The library
+ *     allocates nothing in these calls and keeps no state between calls,
+ *     except the device workspace the caller passes to nvfp4_quantize.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; results are ready when the stream is.
+ *   - Arguments are validated before any HIP call.  The status code is the
+ *     only error channel: nothing is printed, nothing is thrown across the ABI.
+ *     A kernel fault surfaces at the caller's next synchronization.
+ *   - Sizes are int64; every size must be > 0.  Non-contraction dimensions
+ *     may have any size (tails are masked).
+ *   - Calls are reentrant; concurrent calls on different streams are safe as
+ *     long as their output buffers do not overlap.
+ */
+#ifndef FP4_H_
+#define FP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_NULL = 1,    /* a required pointer is NULL                         */
+    FP4_ERR_SHAPE = 2,   /* size <= 0, contraction not a multiple of the block, */
+                         /* or a size whose byte count overflows int64          */
+    FP4_ERR_ALIGN = 3,   /* a pointer is not 16-byte aligned                    */
+    FP4_ERR_ENUM = 4,    /* unknown axis / Hadamard mode / size / rounding      */
+    FP4_ERR_LAUNCH = 5,  /* the HIP runtime refused a kernel launch             */
+    FP4_ERR_WORKSPACE = 6 /* workspace missing or smaller than required         */
+} fp4_status;
+
+/* Which axis of x[rows, cols] the 32-element blocks run along (the GEMM
+ * contraction axis of that operand). */
+typedef enum {
+    FP4_AXIS_COLS = 0,   /* blocks along cols (contiguous): codes [rows, cols/2],
+                            scales [rows, cols/32]                              */
+    FP4_AXIS_ROWS = 1    /* blocks along rows (strided), i.e. quantize x^T:
+                            codes [cols, rows/2], scales [cols, rows/32]        */
+} fp4_axis;
+
+/* Block rotation applied before quantization, along the block axis.
+ * [AMD-MXFP4, "Поисковая экспериментальная работа..."]: a Hadamard transform,
+ * either deterministic (the same every step) or with random sign flips. */
+typedef enum {
+    FP4_HAD_NONE = 0,    /* no rotation                                          */
+    FP4_HAD_DET = 1,     /* y = H_n x / sqrt(n), H_n Sylvester-ordered            */
+    FP4_HAD_SIGNED = 2   /* y = H_n D x / sqrt(n), D = diag of n seeded signs     */
+} fp4_hadamard;
+
+typedef enum {
+    FP4_RTN = 0,         /* nearest E2M1 value, ties to the even code            */
+    FP4_SR = 1           /* stochastic rounding (Philox4x32-10 keyed by sr_seed) */
+} fp4_rounding;
+
+/*
+ * fp4_hadamard_quantize -- rotate (optionally) and quantize bf16 x[rows, cols]
+ * to MXFP4 along `axis`.  [AMD-MXFP4, "Что такое MXFP4"]: 32-element blocks,
+ * one shared E8M0 exponent, E2M1 elements rounded to the nearest value.
+ *
+ * Per 32-element block along the axis (the logical row r of A = x or x^T):
+ *   1. had != NONE: each had_n-element sub-block (had_n = 16 or 32) is
+ *      rotated: a = D x (signs), butterflies with strides 1, 2, ..., had_n/2
+ *      computing (a+b, a-b) in binary32, then one binary32 multiply by
+ *      fl(1/sqrt(had_n)).  D: s_j = -1 iff bit j of word 0 of Philox4x32-10
+ *      (key = sign_seed, counter = (0, 0, 1, 0)); all +1 for DET.
+ *   2. e = clamp(floor(log2 max|y|) - 2, -127, 127) (max = 0 gives -127);
+ *      scale byte = e + 127.  A block holding a NaN or an infinity (also one
+ *      produced by the rotation) gets scale 0xFF and all-zero codes.
+ *   3. v = y * 2^-e in binary32; code = E2M1(v) with saturation at +-6:
+ *      RTN ties to even, or SR: round up iff (u >> 8) * 2^-24 < p, p the
+ *      fractional position between the two neighbours, u = word (idx & 3) of
+ *      Philox4x32-10(key = sr_seed, counter = (idx >> 2, 0, 0) as 32-bit words
+ *      (lo, hi, 0, 0)), idx = r * C + c the element's position in [R, C].
+ *   4. codes: two per byte, the even element in the low nibble.
+ * Output layout: codes [R, C/2], scales [R, C/32] with (R, C) = (rows, cols)
+ * for AXIS_COLS and (cols, rows) for AXIS_ROWS.
+ * Requirements: C % 32 == 0; x, codes, scales 16-byte aligned.
+ * had_n is ignored when had == FP4_HAD_NONE; sign_seed is ignored unless
+ * SIGNED; sr_seed is ignored unless rnd == FP4_SR.  For Wgrad, quantize dY
+ * and X with the same had / had_n / sign_seed so the rotations cancel in
+ * dY^T X (and different sr_seeds).
+ */
+fp4_status fp4_hadamard_quantize(const void* x_bf16, int64_t rows, int64_t cols,
+                                 fp4_axis axis, int had_n, fp4_hadamard had,
+                                 uint64_t sign_seed, fp4_rounding rnd, uint64_t sr_seed,
+                                 uint8_t* codes, uint8_t* scales_e8m0, void* stream);
+
+/*
+ * The three scaled-FP4 GEMMs of a linear layer.  [AMD-MXFP4, "Поисковая
+ * экспериментальная работа: корень нестабильности"]: Fprop Y = X W^T,
+ * Dgrad dX = dY W, Wgrad dW = dY^T X, all in MXFP4 on native FP4 matrix
+ * cores.  Each computes, in fp32 accumulation,
+ *     C[m, n] = sum_k  e2m1(a[m,k]) 2^(sa[m,k/32]-127) * e2m1(b[n,k]) 2^(sb[n,k/32]-127)
+ * over two MXFP4 operands stored along their contraction axis (codes [rows,
+ * Kc/2], scales [rows, Kc/32], as fp4_hadamard_quantize writes them).  C is
+ * written (overwritten, not accumulated) as row-major fp32.
+ * Requirements: T, N, K > 0; the contraction size a multiple of 32; all
+ * pointers 16-byte aligned.
+ */
+/* Fprop:  xq/xs = quantize(X[T,K], AXIS_COLS), wq/ws = quantize(W[N,K], AXIS_COLS);
+ *         y[T, N] = X W^T.  Contraction K. */
+fp4_status fp4_gemm_fprop(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                          const uint8_t* ws, int64_t T, int64_t N, int64_t K,
+                          float* y, void* stream);
+/* Dgrad:  dyq/dys = quantize(dY[T,N], AXIS_COLS), wtq/wts = quantize(W[N,K], AXIS_ROWS);
+ *         dx[T, K] = dY W.  Contraction N. */
+fp4_status fp4_gemm_dgrad(const uint8_t* dyq, const uint8_t* dys, const uint8_t* wtq,
+                          const uint8_t* wts, int64_t T, int64_t N, int64_t K,
+                          float* dx, void* stream);
+/* Wgrad:  dytq/dyts = quantize(dY[T,N], AXIS_ROWS), xtq/xts = quantize(X[T,K], AXIS_ROWS);
+ *         dw[N, K] = dY^T X.  Contraction T. */
+fp4_status fp4_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, const uint8_t* xtq,
+                          const uint8_t* xts, int64_t T, int64_t N, int64_t K,
+                          float* dw, void* stream);
+
+/*
+ * nvfp4_quantize -- NVFP4 quantization of bf16 x[rows, cols] along cols in
+ * 16-element blocks.  [QUARTET-II]: FP4 elements with FP8 (E4M3) block
+ * scales; the renormalization factor of a rotated tensor is folded into the
+ * FP8 scales by stochastic rounding, the elements themselves are rounded to
+ * nearest.  [NV-NVFP4, "Как это работает"]: 16x16 random Hadamard transforms.
+ *   1. y = 16-block transform of each row (had as in fp4_hadamard_quantize
+ *      with had_n = 16; NONE, DET or SIGNED).
+ *   2. A = max |y| over the tensor, or *amax_in (a device float) when
+ *      amax_in != NULL.  s_t = fl(A / 2688) (6 * 448), 1 when A = 0;
+ *      *tensor_scale = s_t (a device float).
+ *   3. per block: s_b = E4M3_RNE(fl(m_b / fl(6 s_t))) saturating at 448;
+ *      s_b = 0 gives all-zero codes and scale 0.  Otherwise
+ *      v_i = y_i * fl(1 / fl(s_b s_t)), codes = E2M1 RTN of v_i.
+ *   4. renorm = 1: num = sum y_i^2, den = sum y_i e2m1(code_i) as binary32
+ *      fmaf chains in element order; if den > 0 the stored scale is
+ *      E4M3_SR(fl(num / fl(s_t den))) with u = word (blk & 3) of
+ *      Philox4x32-10(key = sr_seed, counter = (blk >> 2 as (lo, hi), 2, 0)),
+ *      blk = r * cols/16 + c/16; otherwise s_b.
+ * Layout: codes [rows, cols/2], scales_e4m3 [rows, cols/16].
+ * workspace: device memory of nvfp4_workspace_bytes() bytes, used for the
+ * tensor amax when amax_in == NULL (cleared by the library on `stream`);
+ * may be NULL when amax_in != NULL.  NaN or infinite inputs give
+ * unspecified codes and scales.
+ * Requirements: cols % 16 == 0; pointers 16-byte aligned (tensor_scale and
+ * amax_in 4-byte aligned).
+ */
+fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
+                          uint64_t sign_seed, int renorm, uint64_t sr_seed,
+                          const float* amax_in, uint8_t* codes, uint8_t* scales_e4m3,
+                          float* tensor_scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes nvfp4_quantize needs for a [rows, cols] input. */
+size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols);
+
+/* Static, NUL-terminated name of a status code. */
+const char* fp4_status_string(fp4_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H_ */

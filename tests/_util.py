@@ -1,0 +1,51 @@
+"""Shared test helpers: bf16 bit patterns <-> torch tensors, GPU checks."""
+import numpy as np
+import pytest
+import torch
+
+
+def bf16_bits(values) -> np.ndarray:
+    """bf16 bit patterns (uint16) of float values, rounded to nearest even."""
+    t = torch.tensor(np.asarray(values, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_gpu_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_gpu_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(*args):
+    """Name the case on stdout before a GPU step (flushed, so a fault that
+    ends the process still leaves the case in the log)."""
+    print("[case]", *args, flush=True)
+
+
+def sentinel_u8(shape) -> torch.Tensor:
+    return torch.full(shape, 0xCD, dtype=torch.uint8, device="cuda")
+
+
+def gemm_check(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, tol: float = 1e-5):
+    """|got - ref| <= tol * sum|a b| elementwise; NaN exactly where ref is NaN."""
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan_ref), "NaN pattern differs"
+    g, r, s = got[~nan_ref].astype(np.float64), ref[~nan_ref], mag[~nan_ref]
+    err = np.abs(g - r)
+    bad = err > tol * s
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError("%d of %d entries out of tolerance; e.g. got %s ref %s bound %s"
+                             % (bad.sum(), bad.size, g[i], r[i], tol * s[i]))
+    return float((err / np.maximum(s, 1e-300)).max()) if err.size else 0.0

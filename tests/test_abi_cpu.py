@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: libfp4.so loads, exports every entry point that
+include/fp4.h declares, and rejects bad arguments with the documented status
+codes before making any HIP call (fake pointers below are never touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp4_precision_gemms_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ENUM, ERR_LAUNCH, ERR_WORKSPACE = range(7)
+A = 0x10000          # a fake 16-byte aligned device address (never dereferenced)
+MIS = 0x10008        # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(F.LIB_PATH):
+        pytest.skip("libfp4.so not built")
+    return F.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fp4_hadamard_quantize", "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad",
+              "nvfp4_quantize", "nvfp4_workspace_bytes", "fp4_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", F.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert F.fp4_status_string(s).startswith("FP4_")
+    assert F.fp4_status_string(99) == "FP4_ERR_UNKNOWN"
+
+
+def q(L, x=A, rows=64, cols=64, axis=0, had_n=32, had=1, rnd=0, codes=A, scales=A):
+    return L.fp4_hadamard_quantize(x, rows, cols, axis, had_n, had, 0, rnd, 0, codes, scales, None)
+
+
+def test_quantize_errors(L):
+    assert q(L, axis=2) == ERR_ENUM
+    assert q(L, had=3) == ERR_ENUM
+    assert q(L, had_n=8) == ERR_ENUM
+    assert q(L, rnd=2) == ERR_ENUM
+    assert q(L, x=None) == ERR_NULL
+    assert q(L, codes=None) == ERR_NULL
+    assert q(L, scales=None) == ERR_NULL
+    assert q(L, rows=0) == ERR_SHAPE
+    assert q(L, cols=-32) == ERR_SHAPE
+    assert q(L, cols=48) == ERR_SHAPE                  # contraction along cols
+    assert q(L, rows=48, axis=1) == ERR_SHAPE          # contraction along rows
+    assert q(L, rows=2 ** 40, cols=2 ** 40) == ERR_SHAPE
+    assert q(L, x=MIS) == ERR_ALIGN
+    assert q(L, codes=MIS) == ERR_ALIGN
+    # had_n is not checked when there is no rotation, but the shape still is
+    assert q(L, had=0, had_n=7, cols=40) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", ["fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad"])
+def test_gemm_errors(L, name):
+    fn = getattr(L, name)
+    # contraction dim per role: fprop K, dgrad N, wgrad T
+    contraction = {"fp4_gemm_fprop": 2, "fp4_gemm_dgrad": 1, "fp4_gemm_wgrad": 0}[name]
+
+    def call(ptrs=(A, A, A, A), dims=(64, 64, 64), out=A):
+        return fn(*ptrs, *dims, out, None)
+
+    assert call(ptrs=(None, A, A, A)) == ERR_NULL
+    assert call(ptrs=(A, A, A, None)) == ERR_NULL
+    assert call(out=None) == ERR_NULL
+    for bad in (0, -1):
+        for d in range(3):
+            dims = [64, 64, 64]
+            dims[d] = bad
+            assert call(dims=tuple(dims)) == ERR_SHAPE
+    dims = [64, 64, 64]
+    dims[contraction] = 48
+    assert call(dims=tuple(dims)) == ERR_SHAPE
+    # a non-contraction dim of 48 is fine shape-wise: prove it with a misaligned out
+    dims = [64, 64, 64]
+    dims[(contraction + 1) % 3] = 48
+    assert call(dims=tuple(dims), out=MIS) == ERR_ALIGN
+    assert call(ptrs=(A, MIS, A, A)) == ERR_ALIGN
+
+
+def test_nvfp4_errors(L):
+    def call(x=A, rows=32, cols=64, had=2, renorm=1, amax=None, codes=A, scales=A, ts=A,
+             ws=A, wsb=256):
+        return L.nvfp4_quantize(x, rows, cols, had, 0, renorm, 0, amax, codes, scales, ts, ws, wsb,
+                                None)
+
+    assert call(had=5) == ERR_ENUM
+    assert call(renorm=2) == ERR_ENUM
+    assert call(x=None) == ERR_NULL
+    assert call(ts=None) == ERR_NULL
+    assert call(cols=24) == ERR_SHAPE
+    assert call(rows=0) == ERR_SHAPE
+    assert call(x=MIS) == ERR_ALIGN
+    assert call(ts=A + 2) == ERR_ALIGN
+    assert call(ws=None) == ERR_WORKSPACE
+    assert call(wsb=4) == ERR_WORKSPACE
+    assert L.nvfp4_workspace_bytes(32, 64) >= 4
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    if not os.path.exists(F.LIB_PATH):
+        pytest.skip("libfp4.so not built")
+    with pytest.raises((ValueError, TypeError)):
+        F.fp4_hadamard_quantize(torch.zeros(32, 32, dtype=torch.bfloat16))

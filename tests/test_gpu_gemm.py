@@ -1,0 +1,126 @@
+"""GPU parity of the three scaled-FP4 GEMMs against the oracle's binary64
+product: |C_gpu - C_ref| <= 1e-5 * sum_k |a_mk b_nk| for every entry checked.
+Operands always come from the oracle (random codes and scales, or the
+oracle's quantization of workload tensors), never from the GPU path."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_precision_gemms_amd as F
+import oracle as O
+import workloads as W
+from _util import gemm_check, need_gpu, say, to_gpu_u8
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def rand_operands(rng, rows, K, lo=112, hi=142):
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(lo, hi, (rows, K // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def run(fn, ops, out_shape):
+    need_gpu()
+    g = [to_gpu_u8(a) for a in ops]
+    out = torch.full(out_shape, float("nan"), dtype=torch.float32, device="cuda")
+    fn(*g, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+SHAPES = [(64, 64, 256), (200, 136, 288), (129, 257, 96), (256, 256, 1024), (300, 520, 2080),
+          (1, 1, 32), (33, 31, 64), (512, 384, 4096), (130, 66, 8192 + 32)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_random_operands(M, N, K):
+    rng = np.random.default_rng(M * 131 + N * 7 + K)
+    aq, as_ = rand_operands(rng, M, K)
+    bq, bs = rand_operands(rng, N, K)
+    say("gemm random", M, N, K)
+    got = run(F.fp4_gemm_fprop, (aq, as_, bq, bs), (M, N))
+    ref, mag = O.gemm_rows(aq, as_, bq, bs)
+    gemm_check(got, ref, mag, TOL)
+
+
+def test_gemm_uniform_and_nan_scales():
+    rng = np.random.default_rng(5)
+    M, N, K = 96, 80, 320
+    aq, as_ = rand_operands(rng, M, K)
+    bq, bs = rand_operands(rng, N, K)
+    as_[3, 2] = 0xFF                     # one NaN scale: row 3 of C is NaN
+    bs[10, 0] = 0xFF                     # and column 10
+    as_[7, :] = 0                        # the smallest scale, 2^-127
+    say("gemm nan/extreme scales")
+    got = run(F.fp4_gemm_fprop, (aq, as_, bq, bs), (M, N))
+    ref, mag = O.gemm_rows(aq, as_, bq, bs)
+    gemm_check(got, ref, mag, TOL)
+    assert np.isnan(got[3]).all() and np.isnan(got[:, 10]).all()
+
+
+def _roles(w, had=O.HAD_DET, seed=0):
+    X, dY = W.tensor(w, "X"), W.tensor(w, "dY")
+    out = {"wgrad": (O.quant_mx(dY, O.AXIS_ROWS, 32, had, seed), O.quant_mx(X, O.AXIS_ROWS, 32, had, seed))}
+    if "W" in w.dists:
+        Wt = W.tensor(w, "W")
+        out["fprop"] = (O.quant_mx(X, O.AXIS_COLS), O.quant_mx(Wt, O.AXIS_COLS))
+        out["dgrad"] = (O.quant_mx(dY, O.AXIS_COLS), O.quant_mx(Wt, O.AXIS_ROWS))
+    return out
+
+
+FN = {"fprop": F.fp4_gemm_fprop, "dgrad": F.fp4_gemm_dgrad, "wgrad": F.fp4_gemm_wgrad}
+
+
+def out_shape(w, role):
+    return {"fprop": (w.T, w.N), "dgrad": (w.T, w.K), "wgrad": (w.N, w.K)}[role]
+
+
+@pytest.mark.parametrize("w", [W.WORKLOADS["tiny_wgrad"],
+                               W.scaled(W.WORKLOADS["q_proj"], 512, 384, 320),
+                               W.scaled(W.WORKLOADS["gate_up"], 1024, 256, 448),
+                               W.scaled(W.WORKLOADS["down_proj"], 768, 448, 256)],
+                         ids=lambda w: w.name)
+def test_gemm_roles_workloads(w):
+    for role, ((aq, as_), (bq, bs)) in _roles(w).items():
+        say("gemm", role, w.name)
+        got = run(FN[role], (aq, as_, bq, bs), out_shape(w, role))
+        ref, mag = O.gemm_rows(aq, as_, bq, bs)
+        gemm_check(got, ref, mag, TOL)
+
+
+def test_wgrad_tiny_against_unquantized_product():
+    """Sanity beyond parity: the quantized rotated Wgrad of the tiny workload
+    approximates dY^T X (quantization error, not a parity bound)."""
+    w = W.WORKLOADS["tiny_wgrad"]
+    X, dY = W.tensor(w, "X"), W.tensor(w, "dY")
+    (aq, as_), (bq, bs) = _roles(w)["wgrad"]
+    got = run(F.fp4_gemm_wgrad, (aq, as_, bq, bs), (w.N, w.K))
+    xf = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    df = (dY.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = df.T @ xf
+    mag = np.abs(df).T @ np.abs(xf)
+    assert np.median(np.abs(got - exact) / mag) < 0.05
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", ["gate_up", "q_proj", "down_proj"])
+def test_gemm_full_size_sampled(wname):
+    """Full Llama-3.1-8B shapes through the benchmark's launch: all three
+    GEMMs on oracle-quantized operands, 1024 sampled entries each (corners,
+    tile edges and random positions) recomputed by the oracle."""
+    w = W.WORKLOADS[wname]
+    rng = np.random.default_rng(0)
+    had = O.HAD_SIGNED if wname == "down_proj" else O.HAD_DET
+    roles = _roles(w, had, 77)
+    for role, ((aq, as_), (bq, bs)) in roles.items():
+        M, N = out_shape(w, role)
+        say("full gemm", wname, role, M, N)
+        got = run(FN[role], (aq, as_, bq, bs), (M, N))
+        mi = np.concatenate([[0, 0, M - 1, M - 1, 255, 256], rng.integers(0, M, 1018)])
+        ni = np.concatenate([[0, N - 1, 0, N - 1, 255, 256], rng.integers(0, N, 1018)])
+        ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
+        gemm_check(got[mi, ni], ref, mag, TOL)
+        assert np.isfinite(got).all()

@@ -8,8 +8,10 @@ The pages measure on Llama 3.1-8B pretraining (MLPerf, C4) and on NVFP4 models
 evaluated with MMLU-Pro; neither data nor weights are used.  Tensors of the
 same layer shapes with Gaussian or Student-t values stand in for them.
 
-Generator: numpy PCG64 seeded with SeedSequence([cfg_seed, tensor_id]), values
-drawn in float32 and rounded to bf16 (round-to-nearest-even) by torch.
+Generator: torch's CPU generator seeded with the first 64-bit word of
+numpy's SeedSequence([cfg_seed, tensor_id]); values drawn in float32 and
+rounded to bf16 (round-to-nearest-even).  Student-t with an integer nu is
+drawn by its definition, Z / sqrt(sum of nu squared normals / nu).
 tensor_id: X = 1, W = 2, dY = 3, x (single-tensor configs) = 4.
 """
 from __future__ import annotations
@@ -46,29 +48,37 @@ class Workload:
     seed: int = 0
 
 
-def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+def _generator(seed: int, tensor_id: int) -> torch.Generator:
+    word = np.random.SeedSequence([seed, tensor_id]).generate_state(1, np.uint64)[0]
+    return torch.Generator().manual_seed(int(word) & 0x7FFFFFFFFFFFFFFF)
 
 
 def draw(shape, dist: Dist, seed: int, tensor_id: int) -> np.ndarray:
     """bf16 bit patterns (uint16) of a seeded tensor of `shape`."""
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id])))
+    g = _generator(seed, tensor_id)
     n = int(np.prod(shape))
     if dist.kind == "normal":
-        v = rng.standard_normal(n, dtype=np.float32) * np.float32(dist.std)
+        v = torch.randn(n, generator=g, dtype=torch.float32).mul_(dist.std)
     elif dist.kind == "student_t":
-        v = rng.standard_t(dist.nu, n).astype(np.float32) * np.float32(dist.std)
+        nu = int(dist.nu)
+        if nu != dist.nu or nu < 1:
+            raise ValueError("integer degrees of freedom only")
+        z = torch.randn(n, generator=g, dtype=torch.float32)
+        chi2 = torch.zeros(n, dtype=torch.float32)
+        for _ in range(nu):
+            chi2.addcmul_(*(2 * [torch.randn(n, generator=g, dtype=torch.float32)]))
+        v = z.div_(chi2.div_(nu).sqrt_()).mul_(dist.std)
+        del chi2
     else:
         raise ValueError(dist.kind)
-    v = v.reshape(shape)
+    v = v.view(shape)
     if dist.outlier == "entries":
-        mask = rng.random(n, dtype=np.float32).reshape(shape) < dist.p
-        v[mask] *= np.float32(dist.factor)
+        mask = torch.rand(shape, generator=g) < dist.p
+        v[mask] *= dist.factor
     elif dist.outlier == "channels":
-        cols = rng.permutation(shape[1])[:dist.n_channels]
-        v[:, cols] *= np.float32(dist.factor)
-    return _f32_to_bf16_bits(v)
+        cols = torch.randperm(shape[1], generator=g)[:dist.n_channels]
+        v[:, cols] *= dist.factor
+    return v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def tensor(w: Workload, name: str) -> np.ndarray:
