@@ -16,6 +16,9 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // a * b stays far from int64 overflow (byte counts of bf16 / fp32 tensors)
 bool product_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= (INT64_C(1) << 60) / b; }
 
+constexpr int64_t kMaxContraction = INT64_C(1) << 24;
+constexpr int64_t kMaxTiles = INT64_C(1) << 24;
+
 fp4_status from_hip(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_LAUNCH; }
 
 fp4_status check_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
@@ -24,6 +27,10 @@ fp4_status check_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, c
     if (M <= 0 || N <= 0 || K <= 0 || K % 32) return FP4_ERR_SHAPE;
     if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N) || M > INT32_MAX ||
         N > INT32_MAX)
+        return FP4_ERR_SHAPE;
+    // the kernel addresses a 256-row operand tile with 32-bit byte offsets
+    // and launches one workgroup per 256 x 256 output tile
+    if (K >= kMaxContraction || ((M + 255) / 256) * ((N + 255) / 256) >= kMaxTiles)
         return FP4_ERR_SHAPE;
     if (!aligned16(aq) || !aligned16(as) || !aligned16(bq) || !aligned16(bs) || !aligned16(c))
         return FP4_ERR_ALIGN;

@@ -125,8 +125,9 @@ fp4_status fp4_hadamard_quantize(const void* x_bf16, int64_t rows, int64_t cols,
  * over two MXFP4 operands stored along their contraction axis (codes [rows,
  * Kc/2], scales [rows, Kc/32], as fp4_hadamard_quantize writes them).  C is
  * written (overwritten, not accumulated) as row-major fp32.
- * Requirements: T, N, K > 0; the contraction size a multiple of 32; all
- * pointers 16-byte aligned.
+ * Requirements: T, N, K > 0; the contraction size a multiple of 32 and
+ * below 2^24; at most 2^24 - 1 output tiles of 256 x 256; all pointers
+ * 16-byte aligned.  Otherwise FP4_ERR_SHAPE / FP4_ERR_ALIGN.
  */
 /* Fprop:  xq/xs = quantize(X[T,K], AXIS_COLS), wq/ws = quantize(W[N,K], AXIS_COLS);
  *         y[T, N] = X W^T.  Contraction K. */

@@ -95,6 +95,10 @@ def test_gemm_errors(L, name):
     dims = [64, 64, 64]
     dims[contraction] = 48
     assert call(dims=tuple(dims)) == ERR_SHAPE
+    dims[contraction] = 2 ** 24                        # beyond the 32-bit tile offsets
+    assert call(dims=tuple(dims)) == ERR_SHAPE
+    dims[contraction] = 2 ** 24 - 32
+    assert call(dims=tuple(dims), out=MIS) == ERR_ALIGN
     # a non-contraction dim of 48 is fine shape-wise: prove it with a misaligned out
     dims = [64, 64, 64]
     dims[(contraction + 1) % 3] = 48
