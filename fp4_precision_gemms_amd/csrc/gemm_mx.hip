@@ -51,6 +51,7 @@ constexpr int kScaleBytes = kBK / 32; // scale bytes per row per stage
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0), expcnt/lgkmcnt unchanged
 
 __device__ __forceinline__ int swz(int row, int chunk) {
     return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
@@ -110,7 +111,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int kScA = (BM + BN) * kRowBytes, kScB = kScA + BM * kScaleBytes;
     constexpr int kStage = kScB + BN * kScaleBytes;
     static_assert(BM % 128 == 0 && BN % 128 == 0, "tile sizes");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kStage];
+    // Two stage buffers as distinct arrays: the compiler can then tell that
+    // fragment reads of one do not depend on DMA still landing in the other.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -150,11 +154,17 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
 #pragma unroll
     for (int i = 0; i < SLB; ++i) offsb[i] = (uint32_t)(((wave * SLB + i) * 32 + (lane >> 1)) * ks + (lane & 1) * 4);
 
-    auto load_stage = [&](int kt, int buf) {
-        uint8_t* base = lds + buf * kStage;
-        const int kcode = kt * kRowBytes;
-        // KTAIL: a chunk past the contraction end gets an offset out of range
-        const uint32_t oob = KTAIL ? (uint32_t)(kcode + dchunk * 16 >= kbytes) << 31 : 0u;
+    // A stage kt outside [0, nk) is an all-zero stage (every offset out of
+    // range, zero codes and scale bytes).  Stage -1 lets an odd stage count
+    // run in the loop below, which takes stages two at a time; stage nk is the
+    // (unused) prefetch of the last stage, which keeps every stage one
+    // straight-line block.
+    auto load_stage = [&](int kt, uint8_t* base) {
+        const bool zero = kt < 0 || kt >= nk;
+        const int kcode = zero ? 0 : kt * kRowBytes;
+        // a chunk past the contraction end gets an offset out of range
+        uint32_t oob = zero ? 0x80000000u : 0u;
+        if (KTAIL && !zero) oob = (uint32_t)(kcode + dchunk * 16 >= kbytes) << 31;
 #pragma unroll
         for (int i = 0; i < LA; ++i)
             dma16_to_lds(ra, base + kCodesA + (wave * LA + i) * 8 * kRowBytes, offa[i] | oob, kcode);
@@ -162,21 +172,23 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         for (int i = 0; i < LB; ++i)
             dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * 8 * kRowBytes, offb[i] | oob, kcode);
         if constexpr (!KTAIL) {
-            const int kscale = kt * kScaleBytes;
+            const int kscale = zero ? 0 : kt * kScaleBytes;
 #pragma unroll
             for (int i = 0; i < SLA; ++i)
-                dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * 32 * kScaleBytes, offsa[i], kscale);
+                dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * 32 * kScaleBytes, offsa[i] | oob, kscale);
 #pragma unroll
             for (int i = 0; i < SLB; ++i)
-                dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * 32 * kScaleBytes, offsb[i], kscale);
+                dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * 32 * kScaleBytes, offsb[i] | oob, kscale);
         } else {
             for (int r = tid; r < BM; r += kThreads) {
                 const int64_t g = m0 + r < M ? m0 + r : M - 1;
-                *reinterpret_cast<uint2*>(base + kScA + r * kScaleBytes) = scales8_masked(SA, g, ks, kt);
+                *reinterpret_cast<uint2*>(base + kScA + r * kScaleBytes) =
+                    zero ? make_uint2(0u, 0u) : scales8_masked(SA, g, ks, kt);
             }
             for (int r = tid; r < BN; r += kThreads) {
                 const int64_t g = n0 + r < N ? n0 + r : N - 1;
-                *reinterpret_cast<uint2*>(base + kScB + r * kScaleBytes) = scales8_masked(SB, g, ks, kt);
+                *reinterpret_cast<uint2*>(base + kScB + r * kScaleBytes) =
+                    zero ? make_uint2(0u, 0u) : scales8_masked(SB, g, ks, kt);
             }
         }
     };
@@ -189,49 +201,84 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    load_stage(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
+    // One stage from buffer `base` while stage kt+1 streams into `nbase`:
+    // every wave waits for its own DMA into `base`, then the barrier makes
+    // all of it visible (and frees `nbase`, read one stage earlier).  The
+    // next stage's DMA is issued right after the first fragment reads; the
+    // fragment reads of k-step s+1 are issued ahead of the MFMAs of k-step s.
+    auto run_stage = [&](const uint8_t* base, int kt, uint8_t* nbase) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        const uint8_t* base = lds + buf * kStage;
         const uint8_t* la = base + kCodesA + wm * (BM / 2) * kRowBytes;
         const uint8_t* lb = base + kCodesB + wn * (BN / 2) * kRowBytes;
-        uint4 fa[4][FM], fb[4][FN];
+        // fragments of k-step s live in register set s mod 2
+        uint4 fa[2][FM], fb[2][FN];
         uint2 sa[FM], sb[FN];
+        auto read_frags = [&](int s) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[s & 1][i] = *reinterpret_cast<const uint4*>(la + swz(i * 32 + l32, 2 * s + h));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[s & 1][j] = *reinterpret_cast<const uint4*>(lb + swz(j * 32 + l32, 2 * s + h));
+        };
+        auto mfmas = [&](int s) {
+            const int shift = 8 * (2 * (s & 1) + h);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const uint4 a = fa[s & 1][i];
+                const v8i af = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+                const int sca = (int)(((s < 2 ? sa[i].x : sa[i].y) >> shift) & 0xFFu);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const uint4 b = fb[s & 1][j];
+                    const v8i bf = v8i{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+                    const int scb = (int)(((s < 2 ? sb[j].x : sb[j].y) >> shift) & 0xFFu);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf, af, acc[i][j], 4, 4, 0, scb, 0, sca);
+                }
+            }
+        };
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             sa[i] = *reinterpret_cast<const uint2*>(base + kScA + (wm * (BM / 2) + i * 32 + l32) * kScaleBytes);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
             sb[j] = *reinterpret_cast<const uint2*>(base + kScB + (wn * (BN / 2) + j * 32 + l32) * kScaleBytes);
+        read_frags(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(kt + 1, nbase);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[s][i] = *reinterpret_cast<const uint4*>(la + swz(i * 32 + l32, 2 * s + h));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[s][j] = *reinterpret_cast<const uint4*>(lb + swz(j * 32 + l32, 2 * s + h));
+            if (s < 3) read_frags(s + 1);
+            mfmas(s);
         }
-        if (kt + 1 < nk) load_stage(kt + 1, buf ^ 1);
+        // Issue order: each MFMA is followed by at most one DMA instruction
+        // of the next stage and, every other MFMA, one fragment read of the
+        // next k-step, so neither the DMA burst nor the LDS reads hold up
+        // the matrix pipe.
+        int dma_left = LA + LB + (KTAIL ? 0 : SLA + SLB);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int shift = 8 * (2 * (s & 1) + h);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const v8i af = v8i{(int)fa[s][i].x, (int)fa[s][i].y, (int)fa[s][i].z,
-                                   (int)fa[s][i].w, 0, 0, 0, 0};
-                const int sca = (int)(((s < 2 ? sa[i].x : sa[i].y) >> shift) & 0xFFu);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const v8i bf = v8i{(int)fb[s][j].x, (int)fb[s][j].y, (int)fb[s][j].z,
-                                       (int)fb[s][j].w, 0, 0, 0, 0};
-                    const int scb = (int)(((s < 2 ? sb[j].x : sb[j].y) >> shift) & 0xFFu);
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bf, af, acc[i][j], 4, 4, 0, scb, 0, sca);
+            for (int t = 0; t < FM * FN; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                if (s < 3 && (t & 1) == 0 && t / 2 < FM + FN)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                if (dma_left > 0) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+                    --dma_left;
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int kfirst = -(nk & 1);
+    load_stage(kfirst, lds0);
+    for (int kt = kfirst; kt < nk; kt += 2) {
+        run_stage(lds0, kt, lds1);
+        run_stage(lds1, kt + 1, lds0);
     }
 
     // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
