@@ -17,18 +17,22 @@
 //     block's E8M0 scale.  The B tile is passed as the instruction's first
 //     operand, so the accumulator holds C^T: lane l owns row m = l mod 32 of
 //     C and four runs of four consecutive n, each stored as one 16-byte write.
-//   - A stage is 256 k: 128 code bytes and 8 scale bytes per row.  Both go
-//     global -> LDS by buffer_load ... lds (no VGPR round trip), double
-//     buffered.  One dwordx4 instruction fills 8 rows x 128 code bytes, lane
-//     i writing slot i mod 8 of row i div 8; the lane fetches chunk
-//     (slot XOR row mod 8), so chunk c of row r sits at slot c XOR (r mod 8)
-//     and the 32 rows a fragment read touches spread over all banks.  One
-//     dword instruction fills the 8 scale bytes of 32 rows.  Rows past M
-//     (or N) lie outside the buffer range and read as zero.
-//   - Per stage a wave waits at one barrier, reads all its fragments and
-//     scales of the stage into registers, issues the next stage's DMA into
-//     the other buffer, then runs the stage's MFMAs while that DMA lands.
-//   - A contraction that is not a multiple of 256 (KTAIL) zero-fills the
+//   - A stage is BK k: BK/2 code bytes and BK/32 scale bytes per row.  Both
+//     go global -> LDS by buffer_load ... lds (no VGPR round trip) into a
+//     ring of NBUF stage buffers, NBUF - 1 stages ahead of the MFMAs.  One
+//     dwordx4 instruction fills 64 16-byte slots of consecutive rows, lane i
+//     writing slot i; the lane fetches the chunk that belongs in that slot.
+//     Chunk c of row r sits in slot c XOR ((r / (16 / CPR)) mod CPR), CPR the
+//     chunks per row: the 16 lanes the LDS serves per clock (rows r..r+15 of
+//     one chunk) then hit all 64 banks once.  Dword instructions fill the
+//     scale bytes of 64 / (BK / 128) rows.  Rows past M (or N) lie outside
+//     the buffer range and read as zero.
+//   - Per stage a wave issues the DMA of stage kt + NBUF - 1 and the fragment
+//     reads of its k-steps 1.. between the MFMAs of its k-steps 0.., then
+//     waits for its own DMA of stage kt + 1; one barrier makes that stage
+//     visible to all waves and frees buffer kt; the scales and k-step 0
+//     fragments of stage kt + 1 are read while the last k-step's MFMAs run.
+//   - A contraction that is not a multiple of BK (KTAIL) zero-fills the
 //     missing code chunks through out-of-range offsets and loads the last
 //     stage's scales through registers with the missing blocks set to 127.
 //   - Block order: workgroups are dispatched round-robin over the 8 XCDs;
@@ -41,20 +45,29 @@
 namespace fp4dev {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kBK = 256;              // k elements per stage
-constexpr int kRowBytes = kBK / 2;    // code bytes per row per stage
-constexpr int kScaleBytes = kBK / 32; // scale bytes per row per stage
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
-constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0), expcnt/lgkmcnt unchanged
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+// s_waitcnt immediate: vmcnt(n) with lgkmcnt(0).
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Workgroup barrier without the workgroup-scope release fence of
+// __syncthreads(), which would wait for every outstanding LDS DMA: the caller
+// has already waited (s_waitcnt) for exactly the DMA the barrier publishes.
+// The wavefront-scope fences emit no code; they keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void barrier_after_wait() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Wave-wide DMA: each lane's 16 (or 4) bytes at (voff + soff) of the buffer
@@ -66,6 +79,15 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* 
 __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst,
                                             uint32_t voff, int soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_dst, 4, voff, soff, 0, 0);
+}
+
+// Scaled FP4 MFMA (32x32x64, both operands E2M1, fp32 accumulate) taking the
+// E8M0 scales from byte 0 or byte 2 of the scale registers.
+__device__ __forceinline__ v16f mfma_fp4_byte0(v8i b, v8i a, v16f c, uint32_t sb, uint32_t sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 0, (int)sb, 0, (int)sa);
+}
+__device__ __forceinline__ v16f mfma_fp4_byte2(v8i b, v8i a, v16f c, uint32_t sb, uint32_t sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 2, (int)sb, 2, (int)sa);
 }
 
 // Maps the hardware block index to a (tile_m, tile_n) pair: XCD-contiguous
@@ -83,38 +105,54 @@ __device__ __forceinline__ void tile_of_block(int b, int nb, int tm, int tn, int
     tile_n = r / gm;
 }
 
-// The 8 scale bytes of stage kt of one row, blocks at or past ks read as
-// 127 (2^0; their codes are zero), packed little-endian.
-__device__ __forceinline__ uint2 scales8_masked(const uint8_t* __restrict__ S, int64_t row,
-                                                int64_t ks, int kt) {
-    const int64_t b0 = (int64_t)kt * kScaleBytes;
-    uint32_t b[8];
+// Scale word w (bytes 4w .. 4w+3) of stage kt of one row, SBY scale bytes
+// per row and stage; blocks at or past ks read as 127 (2^0; their codes are
+// zero), packed little-endian.
+template <int SBY>
+__device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict__ S, int64_t row,
+                                                      int64_t ks, int kt, int w) {
+    const int64_t b0 = (int64_t)kt * SBY + 4 * w;
+    uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int64_t c = b0 + i < ks ? b0 + i : ks - 1;
         const uint32_t v = S[row * ks + c];
-        b[i] = b0 + i < ks ? v : 127u;
+        word |= (b0 + i < ks ? v : 127u) << (8 * i);
     }
-    return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                      b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+    return word;
 }
 
-template <int BM, int BN, int GM, bool KTAIL>
+template <int BM, int BN, int BK, int NBUF, int GM, bool KTAIL>
 __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, float* __restrict__ C,
     int tiles_m, int tiles_n) {
-    constexpr int FM = BM / 64, FN = BN / 64;          // 32x32 tiles per wave
-    constexpr int LA = BM / 32, LB = BN / 32;          // code DMA instructions per wave per stage
-    constexpr int SLA = BM / 128, SLB = BN / 128;      // scale DMA instructions per wave per stage
-    constexpr int kCodesA = 0, kCodesB = BM * kRowBytes;
-    constexpr int kScA = (BM + BN) * kRowBytes, kScB = kScA + BM * kScaleBytes;
-    constexpr int kStage = kScB + BN * kScaleBytes;
-    static_assert(BM % 128 == 0 && BN % 128 == 0, "tile sizes");
-    // Two stage buffers as distinct arrays: the compiler can then tell that
-    // fragment reads of one do not depend on DMA still landing in the other.
+    constexpr int RB = BK / 2;                     // code bytes per row per stage
+    constexpr int CPR = RB / 16;                   // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                  // rows per code DMA instruction
+    constexpr int SWZ = 16 / CPR;                  // rows sharing a swizzle value
+    constexpr int SBY = BK / 32;                   // scale bytes per row per stage
+    constexpr int SW = SBY / 4;                    // scale words per row per stage
+    constexpr int SRPI = 64 / SW;                  // rows per scale DMA instruction
+    constexpr int KS = BK / 64;                    // MFMA k-steps per stage
+    constexpr int FM = BM / 64, FN = BN / 64;      // 32x32 tiles per wave
+    constexpr int LA = BM / RPI / 4, LB = BN / RPI / 4;      // code DMAs per wave per stage
+    constexpr int SLA = BM / SRPI / 4, SLB = BN / SRPI / 4;  // scale DMAs per wave per stage
+    constexpr int DMA_PER_STAGE = LA + LB + (KTAIL ? 0 : SLA + SLB);
+    constexpr int kCodesA = 0, kCodesB = BM * RB;
+    constexpr int kScA = (BM + BN) * RB, kScB = kScA + BM * SBY;
+    constexpr int kStage = kScB + BN * SBY;
+    constexpr int D = NBUF - 1;                    // stages of DMA in flight
+    static_assert(BK == 128 || BK == 256, "stage depth");
+    static_assert(NBUF == 2 || NBUF == 4, "stage ring");
+    static_assert(BM % 256 == 0 && BN % 256 == 0, "tile sizes");
+    static_assert(NBUF * kStage <= 160 * 1024, "LDS");
+    // Stage buffers as distinct arrays: the compiler can then tell that
+    // fragment reads of one do not wait on DMA still landing in another.
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[NBUF > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NBUF > 2 ? kStage : 16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -125,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     tile_n = __builtin_amdgcn_readfirstlane(tile_n);
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
     const int64_t kbytes = K / 2, ks = K / 32;
-    const int nk = (int)((K + kBK - 1) / kBK);
+    const int nk = (int)((K + BK - 1) / BK);
 
     // Buffer views of this block's rows: rows past M / N are out of range.
     const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
@@ -140,55 +178,73 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         (void*)(SB + n0 * ks), (short)0, (int)(rows_b * ks), kBufferWord3);
 
     // Per-lane DMA offsets within the stage at k = 0; the stage's k offset
-    // goes in the scalar offset.  Codes: row lane/8 of an 8-row group, chunk
-    // (lane mod 8) XOR (lane / 8).  Scales: row lane/2 of a 32-row group,
-    // bytes 4 (lane mod 2) .. +3.
-    const int drow = lane >> 3, dchunk = (lane & 7) ^ drow;
+    // goes in the scalar offset.  Codes: row lane / CPR of an RPI-row group,
+    // the chunk that belongs in slot lane mod CPR of that row.  Scales: row
+    // lane / SW of an SRPI-row group, scale word lane mod SW.
+    const int drow = lane / CPR, dslot = lane % CPR;
     uint32_t offa[LA], offb[LB], offsa[SLA], offsb[SLB];
+    int chka[LA], chkb[LB];   // byte offset of the fetched chunk within the row
 #pragma unroll
-    for (int i = 0; i < LA; ++i) offa[i] = (uint32_t)(((wave * LA + i) * 8 + drow) * kbytes + dchunk * 16);
+    for (int i = 0; i < LA; ++i) {
+        const int row = (wave * LA + i) * RPI + drow;
+        chka[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
+        offa[i] = (uint32_t)(row * kbytes + chka[i]);
+    }
 #pragma unroll
-    for (int i = 0; i < LB; ++i) offb[i] = (uint32_t)(((wave * LB + i) * 8 + drow) * kbytes + dchunk * 16);
+    for (int i = 0; i < LB; ++i) {
+        const int row = (wave * LB + i) * RPI + drow;
+        chkb[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
+        offb[i] = (uint32_t)(row * kbytes + chkb[i]);
+    }
 #pragma unroll
-    for (int i = 0; i < SLA; ++i) offsa[i] = (uint32_t)(((wave * SLA + i) * 32 + (lane >> 1)) * ks + (lane & 1) * 4);
+    for (int i = 0; i < SLA; ++i)
+        offsa[i] = (uint32_t)(((wave * SLA + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
 #pragma unroll
-    for (int i = 0; i < SLB; ++i) offsb[i] = (uint32_t)(((wave * SLB + i) * 32 + (lane >> 1)) * ks + (lane & 1) * 4);
+    for (int i = 0; i < SLB; ++i)
+        offsb[i] = (uint32_t)(((wave * SLB + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
 
     // A stage kt outside [0, nk) is an all-zero stage (every offset out of
-    // range, zero codes and scale bytes).  Stage -1 lets an odd stage count
-    // run in the loop below, which takes stages two at a time; stage nk is the
-    // (unused) prefetch of the last stage, which keeps every stage one
-    // straight-line block.
+    // range, zero codes and scale bytes).  Leading zero stages round the
+    // stage count up to a multiple of NBUF for the loop below; trailing ones
+    // are the (unused) prefetches past the last stage, which keep every
+    // stage one straight-line block.
     auto load_stage = [&](int kt, uint8_t* base) {
         const bool zero = kt < 0 || kt >= nk;
-        const int kcode = zero ? 0 : kt * kRowBytes;
+        const int kcode = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * RB);
         // a chunk past the contraction end gets an offset out of range
-        uint32_t oob = zero ? 0x80000000u : 0u;
-        if (KTAIL && !zero) oob = (uint32_t)(kcode + dchunk * 16 >= kbytes) << 31;
+        const uint32_t oob = zero ? 0x80000000u : 0u;
 #pragma unroll
-        for (int i = 0; i < LA; ++i)
-            dma16_to_lds(ra, base + kCodesA + (wave * LA + i) * 8 * kRowBytes, offa[i] | oob, kcode);
+        for (int i = 0; i < LA; ++i) {
+            const uint32_t tail = KTAIL ? (uint32_t)(kcode + chka[i] >= kbytes) << 31 : 0u;
+            dma16_to_lds(ra, base + kCodesA + (wave * LA + i) * RPI * RB, offa[i] | oob | tail, kcode);
+        }
 #pragma unroll
-        for (int i = 0; i < LB; ++i)
-            dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * 8 * kRowBytes, offb[i] | oob, kcode);
+        for (int i = 0; i < LB; ++i) {
+            const uint32_t tail = KTAIL ? (uint32_t)(kcode + chkb[i] >= kbytes) << 31 : 0u;
+            dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * RPI * RB, offb[i] | oob | tail, kcode);
+        }
         if constexpr (!KTAIL) {
-            const int kscale = zero ? 0 : kt * kScaleBytes;
+            const int kscale = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * SBY);
 #pragma unroll
             for (int i = 0; i < SLA; ++i)
-                dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * 32 * kScaleBytes, offsa[i] | oob, kscale);
+                dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * SRPI * SBY, offsa[i] | oob, kscale);
 #pragma unroll
             for (int i = 0; i < SLB; ++i)
-                dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * 32 * kScaleBytes, offsb[i] | oob, kscale);
+                dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, kscale);
         } else {
             for (int r = tid; r < BM; r += kThreads) {
                 const int64_t g = m0 + r < M ? m0 + r : M - 1;
-                *reinterpret_cast<uint2*>(base + kScA + r * kScaleBytes) =
-                    zero ? make_uint2(0u, 0u) : scales8_masked(SA, g, ks, kt);
+#pragma unroll
+                for (int w = 0; w < SW; ++w)
+                    reinterpret_cast<uint32_t*>(base + kScA + r * SBY)[w] =
+                        zero ? 0u : scale_word_masked<SBY>(SA, g, ks, kt, w);
             }
             for (int r = tid; r < BN; r += kThreads) {
                 const int64_t g = n0 + r < N ? n0 + r : N - 1;
-                *reinterpret_cast<uint2*>(base + kScB + r * kScaleBytes) =
-                    zero ? make_uint2(0u, 0u) : scales8_masked(SB, g, ks, kt);
+#pragma unroll
+                for (int w = 0; w < SW; ++w)
+                    reinterpret_cast<uint32_t*>(base + kScB + r * SBY)[w] =
+                        zero ? 0u : scale_word_masked<SBY>(SB, g, ks, kt, w);
             }
         }
     };
@@ -201,85 +257,124 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // One stage from buffer `base` while stage kt+1 streams into `nbase`:
-    // every wave waits for its own DMA into `base`, then the barrier makes
-    // all of it visible (and frees `nbase`, read one stage earlier).  The
-    // next stage's DMA is issued right after the first fragment reads; the
-    // fragment reads of k-step s+1 are issued ahead of the MFMAs of k-step s.
-    auto run_stage = [&](const uint8_t* base, int kt, uint8_t* nbase) {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        const uint8_t* la = base + kCodesA + wm * (BM / 2) * kRowBytes;
-        const uint8_t* lb = base + kCodesB + wn * (BN / 2) * kRowBytes;
-        // fragments of k-step s live in register set s mod 2
-        uint4 fa[2][FM], fb[2][FN];
-        uint2 sa[FM], sb[FN];
-        auto read_frags = [&](int s) {
+    // Register state: the fragments of two k-steps (k-step s in set s mod 2)
+    // and the scale words of two stages (word w of a fragment row holds the
+    // blocks of k-steps 2w and 2w+1).  Shifted right by 8 h, word s / 2 holds
+    // this lane's block of k-step s in byte 0 (even s) or byte 2 (odd s),
+    // which the MFMA selects by op_sel.
+    struct Scales { uint32_t a[FM][SW], b[FN][SW]; };
+    // native vectors (not HIP's uint4 struct): one 16-byte LDS load each
+    v4i fa[2][FM], fb[2][FN];
+    auto read_frags = [&](const uint8_t* base, int s) {
+        const uint8_t* la = base + kCodesA + wm * (BM / 2) * RB;
+        const uint8_t* lb = base + kCodesB + wn * (BN / 2) * RB;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[s & 1][i] = *reinterpret_cast<const uint4*>(la + swz(i * 32 + l32, 2 * s + h));
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[s & 1][j] = *reinterpret_cast<const uint4*>(lb + swz(j * 32 + l32, 2 * s + h));
-        };
-        auto mfmas = [&](int s) {
-            const int shift = 8 * (2 * (s & 1) + h);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const uint4 a = fa[s & 1][i];
-                const v8i af = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-                const int sca = (int)(((s < 2 ? sa[i].x : sa[i].y) >> shift) & 0xFFu);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const uint4 b = fb[s & 1][j];
-                    const v8i bf = v8i{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-                    const int scb = (int)(((s < 2 ? sb[j].x : sb[j].y) >> shift) & 0xFFu);
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bf, af, acc[i][j], 4, 4, 0, scb, 0, sca);
-                }
-            }
-        };
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            sa[i] = *reinterpret_cast<const uint2*>(base + kScA + (wm * (BM / 2) + i * 32 + l32) * kScaleBytes);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            sb[j] = *reinterpret_cast<const uint2*>(base + kScB + (wn * (BN / 2) + j * 32 + l32) * kScaleBytes);
-        read_frags(0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_stage(kt + 1, nbase);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (s < 3) read_frags(s + 1);
-            mfmas(s);
+        for (int i = 0; i < FM; ++i) {
+            const int row = i * 32 + l32;
+            fa[s & 1][i] = *reinterpret_cast<const v4i*>(
+                la + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
         }
-        // Issue order: each MFMA is followed by at most one DMA instruction
-        // of the next stage and, every other MFMA, one fragment read of the
-        // next k-step, so neither the DMA burst nor the LDS reads hold up
-        // the matrix pipe.
-        int dma_left = LA + LB + (KTAIL ? 0 : SLA + SLB);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int j = 0; j < FN; ++j) {
+            const int row = j * 32 + l32;
+            fb[s & 1][j] = *reinterpret_cast<const v4i*>(
+                lb + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
+        }
+    };
+    auto read_scales = [&](const uint8_t* base, Scales& sc) {
 #pragma unroll
-            for (int t = 0; t < FM * FN; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-                if (s < 3 && (t & 1) == 0 && t / 2 < FM + FN)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                if (dma_left > 0) {
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-                    --dma_left;
-                }
+        for (int i = 0; i < FM; ++i) {
+            const uint8_t* p = base + kScA + (wm * (BM / 2) + i * 32 + l32) * SBY;
+#pragma unroll
+            for (int w = 0; w < SW; ++w) sc.a[i][w] = reinterpret_cast<const uint32_t*>(p)[w];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const uint8_t* p = base + kScB + (wn * (BN / 2) + j * 32 + l32) * SBY;
+#pragma unroll
+            for (int w = 0; w < SW; ++w) sc.b[j][w] = reinterpret_cast<const uint32_t*>(p)[w];
+        }
+    };
+    auto mfmas = [&](int s, const Scales& sc) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const v8i af = __builtin_shufflevector(fa[s & 1][i], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+            const uint32_t wa = sc.a[i][s >> 1] >> (8 * h);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const v8i bf = __builtin_shufflevector(fb[s & 1][j], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+                const uint32_t wb = sc.b[j][s >> 1] >> (8 * h);
+                acc[i][j] = (s & 1) ? mfma_fp4_byte2(bf, af, acc[i][j], wb, wa)
+                                    : mfma_fp4_byte0(bf, af, acc[i][j], wb, wa);
             }
+        }
+    };
+
+    // One stage from buffer `cur` (its k-step 0 fragments and scales already
+    // in registers as `sc`); `ahead` receives stage kt + D, `next` holds
+    // stage kt + 1.
+    auto run_stage = [&](const uint8_t* cur, int kt, uint8_t* ahead, const uint8_t* next,
+                         const Scales& sc, Scales& nsc) {
+        load_stage(kt + D, ahead);
+#pragma unroll
+        for (int s = 0; s < KS - 1; ++s) {
+            read_frags(cur, s + 1);
+            mfmas(s, sc);
+        }
+        int dma_left = DMA_PER_STAGE;
+        int ds_left = (KS - 1) * (FM + FN);
+#pragma unroll
+        for (int t = 0; t < (KS - 1) * FM * FN; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+            if (dma_left > 0) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
+                --dma_left;
+            }
+            if ((t & 1) == 0 && ds_left > 0) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                --ds_left;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's DMA of stage kt + 1 has landed (only the D - 1 younger
+        // stages may still be in flight) and its reads of `cur` are done
+        if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
+        barrier_after_wait();
+        read_scales(next, nsc);
+        read_frags(next, 0);
+        mfmas(KS - 1, sc);
+#pragma unroll
+        for (int t = 0; t < FM * FN; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    const int kfirst = -(nk & 1);
-    load_stage(kfirst, lds0);
-    for (int kt = kfirst; kt < nk; kt += 2) {
-        run_stage(lds0, kt, lds1);
-        run_stage(lds1, kt + 1, lds0);
+    uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
+    const int kfirst = -((NBUF - nk % NBUF) % NBUF);
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
+    if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
+    barrier_after_wait();
+    Scales sc0, sc1;
+    read_scales(bufs[0], sc0);
+    read_frags(bufs[0], 0);
+    for (int kt = kfirst; kt < nk; kt += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            if (b & 1)
+                run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc1, sc0);
+            else
+                run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc0, sc1);
+        }
     }
+
+    // the prefetches past the last stage must land before the workgroup
+    // (and its LDS) goes away
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
     // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
     // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.
@@ -309,13 +404,18 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     }
 }
 
-template <int BM, int BN, int GM, bool KTAIL>
+template <int BM, int BN, int BK, int NBUF, int GM>
 hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
                         const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
                         hipStream_t st) {
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_mx_tn<BM, BN, GM, KTAIL>), dim3((unsigned)(tm * tn)), dim3(kThreads),
-                       0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+    if (K % BK == 0) {
+        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, BK, NBUF, GM, false>), dim3((unsigned)(tm * tn)),
+                           dim3(kThreads), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+    } else {
+        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, BK, NBUF, GM, true>), dim3((unsigned)(tm * tn)),
+                           dim3(kThreads), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+    }
     return hipGetLastError();
 }
 
@@ -324,8 +424,11 @@ hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
                           hipStream_t st) {
-    if (K % kBK == 0) return launch_tiles<256, 256, 8, false>(aq, as, bq, bs, M, N, K, c, st);
-    return launch_tiles<256, 256, 8, true>(aq, as, bq, bs, M, N, K, c, st);
+#ifndef FP4_GEMM_BK
+#define FP4_GEMM_BK 256
+#define FP4_GEMM_NBUF 2
+#endif
+    return launch_tiles<256, 256, FP4_GEMM_BK, FP4_GEMM_NBUF, 8>(aq, as, bq, bs, M, N, K, c, st);
 }
 
 }  // namespace fp4dev
