@@ -15,10 +15,21 @@
 //     two-step DPP reduction, and each lane stores its 8 codes as one dword.
 //   quant_mx_along_rows -- blocks run along the strided dim (x^T is
 //     quantized, as Wgrad needs: blocks along tokens).  A lane owns CPL
-//     adjacent columns and a 32-row block of each: it issues 32 row loads
-//     (adjacent lanes read adjacent columns, so every load instruction reads
-//     one contiguous 64*CPL*2-byte row segment), then transforms, reduces and
-//     encodes each column entirely in registers and stores 16 code bytes.
+//     adjacent columns and RBW consecutive 32-row blocks of each: per block
+//     it issues 32 row loads (adjacent lanes read adjacent columns, so every
+//     load instruction reads one contiguous 64*CPL*2-byte row segment), then
+//     transforms, reduces and encodes each column in registers; its RBW
+//     blocks of one column are 16*RBW contiguous code bytes.
+//
+// Element encoding.  The block maximum is taken on the butterfly outputs a_i
+// before the binary32 multiply by c = fl(1/sqrt(n)): rounding is monotone,
+// so max_i |fl(c a_i)| = fl(c max_i |a_i|).  With the scale 2^e normal
+// (scale byte 1..254) the codes come from V_CVT_SCALEF32_PK_FP4_F32, which
+// rounds y / 2^e to the nearest E2M1 value, ties to even, saturating at 6 --
+// for a power-of-two scale the same code as rounding the exact binary32
+// product y * 2^-e; two elements per instruction, packed even-low.  Scale
+// byte 0 (2^-127, not a normal binary32) and stochastic rounding take the
+// integer encoders of fp4_device.hpp.
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
@@ -35,12 +46,13 @@ __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
 __device__ __forceinline__ float quad_xor1f(float v) { return __uint_as_float(quad_xor1(__float_as_uint(v))); }
 __device__ __forceinline__ float quad_xor2f(float v) { return __uint_as_float(quad_xor2(__float_as_uint(v))); }
 
-// In-register butterflies with strides 1, 2, 4 over a[0..7].
-__device__ __forceinline__ void butterfly8(float* a) {
+// In-register butterflies with strides 1 .. N/2 over a[0..N-1].
+template <int N>
+__device__ __forceinline__ void butterflies(float* a) {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int h = 1; h < N; h <<= 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < N; ++i) {
             if (i & h) continue;
             const float x = a[i], y = a[i + h];
             a[i] = x + y;
@@ -49,9 +61,31 @@ __device__ __forceinline__ void butterfly8(float* a) {
     }
 }
 
-// Encodes 8 rotated values of one lane into 8 nibbles (element 0 lowest).
+// Largest |a_i| of n values as binary32 bits (NaN > Inf > finite).
+template <int N>
+__device__ __forceinline__ uint32_t max_abs_bits(const float* a) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int t = 0; t < N; ++t) m = max(m, __float_as_uint(a[t]) & 0x7FFFFFFFu);
+    return m;
+}
+
+// Codes of 8 values y[0..7] under scale byte `byte` (1..254): hardware
+// round-to-nearest-even of y / 2^(byte-127), element 2k in nibble 2k.
+__device__ __forceinline__ uint32_t encode8_hw(const float* y, uint32_t byte) {
+    const float s = __uint_as_float(byte << 23);
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], s, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], s, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], s, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], s, 3);
+    return w;
+}
+
+// Integer encoders: v_t = y_t * 2^-(byte-127) in binary32, then RTN or SR.
 template <bool SR>
-__device__ __forceinline__ uint32_t encode8(const float* y, float inv, uint4 u0, uint4 u1) {
+__device__ __forceinline__ uint32_t encode8_sw(const float* y, uint32_t byte, uint4 u0, uint4 u1) {
+    const float inv = inv_scale_from_e8m0(byte);
     uint32_t w = 0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -80,6 +114,9 @@ __global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
         if (g[u] < nchunks) w[u] = x[g[u]];
     }
     const int q = threadIdx.x & 3;                 // lane within the block of 4
+    // sign-bit masks of the cross-lane butterfly stages: the upper lane of a
+    // pair computes partner - own as partner + (-own)
+    const uint32_t neg1 = (uint32_t)(q & 1) << 31, neg2 = (uint32_t)((q >> 1) & 1) << 31;
 #pragma unroll
     for (int u = 0; u < kColsUnroll; ++u) {
         if (g[u] >= nchunks) break;                // uniform per quad: nchunks % 4 == 0
@@ -89,38 +126,39 @@ __global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
             const int sbase = (8 * q) % HADN;
 #pragma unroll
             for (int t = 0; t < 8; ++t) a[t] = flip_if(a[t], (sign_word >> (sbase + t)) & 1u);
-            butterfly8(a);
-            // stride 8: pair (i, i+8) lives in lanes (q, q^1); the lower lane adds
+            butterflies<8>(a);
+            // stride 8: pair (i, i+8) lives in lanes (q, q^1)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float p = quad_xor1f(a[t]);
-                a[t] = (q & 1) ? (p - a[t]) : (a[t] + p);
-            }
+            for (int t = 0; t < 8; ++t)
+                a[t] = quad_xor1f(a[t]) + __uint_as_float(__float_as_uint(a[t]) ^ neg1);
             if constexpr (HADN == 32) {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float p = quad_xor2f(a[t]);
-                    a[t] = (q & 2) ? (p - a[t]) : (a[t] + p);
-                }
+                for (int t = 0; t < 8; ++t)
+                    a[t] = quad_xor2f(a[t]) + __uint_as_float(__float_as_uint(a[t]) ^ neg2);
             }
+        }
+        // block maximum of |a| as unsigned bits, then of |c a| (monotone rounding)
+        uint32_t m = max_abs_bits<8>(a);
+        m = max(m, quad_xor1(m));
+        m = max(m, quad_xor2(m));
+        if constexpr (HADN != 0) {
+            m = __float_as_uint(__uint_as_float(m) * norm) & 0x7FFFFFFFu;
 #pragma unroll
             for (int t = 0; t < 8; ++t) a[t] = a[t] * norm;
         }
-        // block maximum of |y| as unsigned bits (NaN > Inf > finite)
-        uint32_t m = 0;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(a[t]) & 0x7FFFFFFFu);
-        m = max(m, quad_xor1(m));
-        m = max(m, quad_xor2(m));
         const uint32_t byte = e8m0_from_amax_bits(m);
         uint32_t word = 0;
         if (byte != 255u) {
-            uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
-            if constexpr (SR) {
-                u0 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2);
-                u1 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2 + 1);
+            if (!SR && byte != 0u) {
+                word = encode8_hw(a, byte);
+            } else {
+                uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+                if constexpr (SR) {
+                    u0 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2);
+                    u1 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2 + 1);
+                }
+                word = encode8_sw<SR>(a, byte, u0, u1);
             }
-            word = encode8<SR>(a, inv_scale_from_e8m0(byte), u0, u1);
         }
         codes[g[u]] = word;
         if (q == 0) scales[g[u] >> 2] = (uint8_t)byte;
@@ -131,13 +169,19 @@ template <int CPL> struct ColVec;
 template <> struct ColVec<1> { using T = uint16_t; };
 template <> struct ColVec<2> { using T = uint32_t; };
 template <> struct ColVec<4> { using T = uint2; };
+template <> struct ColVec<8> { using T = uint4; };
 
 template <int CPL>
 __device__ __forceinline__ float col_value(const typename ColVec<CPL>::T& v, int c) {
-    if constexpr (CPL == 1) return __uint_as_float((uint32_t)v << 16);
-    else if constexpr (CPL == 2) return c == 0 ? bf16_lo(v) : bf16_hi(v);
-    else {
+    if constexpr (CPL == 1) {
+        return __uint_as_float((uint32_t)v << 16);
+    } else if constexpr (CPL == 2) {
+        return c == 0 ? bf16_lo(v) : bf16_hi(v);
+    } else if constexpr (CPL == 4) {
         const uint32_t w = c < 2 ? v.x : v.y;
+        return (c & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+        const uint32_t w = c < 2 ? v.x : c < 4 ? v.y : c < 6 ? v.z : v.w;
         return (c & 1) ? bf16_hi(w) : bf16_lo(w);
     }
 }
@@ -155,12 +199,12 @@ __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
     if (col0 >= cols) return;                      // no cross-lane work in this kernel
     const int64_t nrb = rows / 32;
     const int64_t rb0 = ((int64_t)blockIdx.y * kRowsWaves + wave) * RBW;
+    const int64_t vstride = cols / CPL;
     for (int i = 0; i < RBW; ++i) {
         const int64_t rb = rb0 + i;
         if (rb >= nrb) break;
         V v[32];
         const V* src = reinterpret_cast<const V*>(x + rb * 32 * cols + col0);
-        const int64_t vstride = cols / CPL;
 #pragma unroll
         for (int r = 0; r < 32; ++r) v[r] = src[r * vstride];
 #pragma unroll
@@ -172,36 +216,33 @@ __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
 #pragma unroll
                 for (int r = 0; r < 32; ++r) a[r] = flip_if(a[r], (sign_word >> (r % HADN)) & 1u);
 #pragma unroll
-                for (int h = 1; h < HADN; h <<= 1) {
-#pragma unroll
-                    for (int r = 0; r < 32; ++r) {
-                        if (r & h) continue;
-                        const float p = a[r], s = a[r + h];
-                        a[r] = p + s;
-                        a[r + h] = p - s;
-                    }
-                }
+                for (int o = 0; o < 32; o += HADN) butterflies<HADN>(a + o);
+            }
+            uint32_t m = max_abs_bits<32>(a);
+            if constexpr (HADN != 0) {
+                m = __float_as_uint(__uint_as_float(m) * norm) & 0x7FFFFFFFu;
 #pragma unroll
                 for (int r = 0; r < 32; ++r) a[r] = a[r] * norm;
             }
-            uint32_t m = 0;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) m = max(m, __float_as_uint(a[r]) & 0x7FFFFFFFu);
             const uint32_t byte = e8m0_from_amax_bits(m);
             const int64_t col = col0 + c;
             uint4 out = make_uint4(0, 0, 0, 0);
             if (byte != 255u) {
-                const float inv = inv_scale_from_e8m0(byte);
-                const uint64_t gbase = ((uint64_t)col * (uint64_t)rows + (uint64_t)rb * 32) >> 2;
                 uint32_t wd[4];
+                if (!SR && byte != 0u) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
-                    if constexpr (SR) {
-                        u0 = stream4(sr_seed, 0u, gbase + 2 * k);
-                        u1 = stream4(sr_seed, 0u, gbase + 2 * k + 1);
+                    for (int k = 0; k < 4; ++k) wd[k] = encode8_hw(a + 8 * k, byte);
+                } else {
+                    const uint64_t gbase = ((uint64_t)col * (uint64_t)rows + (uint64_t)rb * 32) >> 2;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+                        if constexpr (SR) {
+                            u0 = stream4(sr_seed, 0u, gbase + 2 * k);
+                            u1 = stream4(sr_seed, 0u, gbase + 2 * k + 1);
+                        }
+                        wd[k] = encode8_sw<SR>(a + 8 * k, byte, u0, u1);
                     }
-                    wd[k] = encode8<SR>(a + 8 * k, inv, u0, u1);
                 }
                 out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
             }
