@@ -188,18 +188,25 @@ __device__ __forceinline__ float col_value(const typename ColVec<CPL>::T& v, int
 
 constexpr int kRowsWaves = 4;
 
-// One lane: CPL columns x RBW consecutive 32-row blocks.
+// One lane: CPL columns x RBW consecutive 32-row blocks.  The RBW scale
+// bytes of a column are contiguous and leave as one RBW-byte store.
 template <int CPL, int HADN, bool SR, int RBW>
 __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
     uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    static_assert(RBW == 4, "scale bytes of a lane are packed into one word");
     using V = typename ColVec<CPL>::T;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t col0 = ((int64_t)blockIdx.x * 64 + lane) * CPL;
     if (col0 >= cols) return;                      // no cross-lane work in this kernel
     const int64_t nrb = rows / 32;
     const int64_t rb0 = ((int64_t)blockIdx.y * kRowsWaves + wave) * RBW;
+    if (rb0 >= nrb) return;
     const int64_t vstride = cols / CPL;
+    uint32_t sword[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) sword[c] = 0;
+#pragma unroll
     for (int i = 0; i < RBW; ++i) {
         const int64_t rb = rb0 + i;
         if (rb >= nrb) break;
@@ -247,8 +254,140 @@ __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
                 out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
             }
             *reinterpret_cast<uint4*>(codes + col * (rows / 2) + rb * 16) = out;
-            scales[col * (rows / 32) + rb] = (uint8_t)byte;
+            sword[c] |= byte << (8 * i);
         }
+    }
+    // scale bytes rb0 .. rb0+3 of each column: one aligned word when all four
+    // blocks exist and the row of scales is a multiple of 4 bytes
+    const bool word_ok = rb0 + RBW <= nrb && (nrb % 4) == 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        uint8_t* dst = scales + (col0 + c) * nrb + rb0;
+        if (word_ok) {
+            *reinterpret_cast<uint32_t*>(dst) = sword[c];
+        } else {
+            for (int i = 0; i < RBW && rb0 + i < nrb; ++i) dst[i] = (uint8_t)(sword[c] >> (8 * i));
+        }
+    }
+}
+
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wave-wide DMA: each lane's 16 bytes at voff of the buffer go to LDS at
+// lds_dst + 16 * lane (lds_dst wave-uniform).
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+}
+
+constexpr int kTileCols = 256;           // columns per block, one per thread
+constexpr int kTileBlocks = 4;           // 32-row blocks per workgroup
+constexpr int kTileBytes = 32 * kTileCols * 2;
+
+// Blocks along rows, staged through LDS: a workgroup owns 256 adjacent
+// columns and 4 consecutive 32-row blocks.  All four 32 x 256 bf16 tiles go
+// global -> LDS by DMA up front (each wave instruction moves two 512-byte
+// row segments); tile t is processed once its DMA has landed.  Thread c
+// owns column c: it reads the column's 32 values of a tile from LDS
+// (consecutive lanes, consecutive columns: conflict-free), transforms and
+// encodes them, and at the end stores its 4 blocks' codes as 64 contiguous
+// bytes and their scales as one 4-byte word.  Needs cols % 8 == 0.
+template <int HADN, bool SR>
+__global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
+    uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    __shared__ __attribute__((aligned(1024))) uint16_t tile[kTileBlocks][32 * kTileCols];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t c0 = (int64_t)__builtin_amdgcn_readfirstlane((int)blockIdx.x) * kTileCols;
+    const int64_t nrb = rows / 32;
+    const int64_t rb0 = (int64_t)__builtin_amdgcn_readfirstlane((int)blockIdx.y) * kTileBlocks;
+    const int nt = (int)((nrb - rb0) < kTileBlocks ? (nrb - rb0) : kTileBlocks);
+    // the whole input as one buffer: offsets are 32-bit, the caller bounds
+    // rows * cols * 2 below 2^31; segments past the last row read as zero
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)x, (short)0, (int)(rows * cols * 2), 0x00020000);
+    // DMA instruction j of a tile (4 per wave) covers rows 2j, 2j+1:
+    // lane i -> row 2j + i / 32, bytes 16 (i mod 32) of the row segment.
+    // Every tile is issued, also those past the last row (they read zeros),
+    // so that the wait counts below are the same for every workgroup.
+    const int64_t nbytes = rows * cols * 2;
+#pragma unroll
+    for (int t = 0; t < kTileBlocks; ++t) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = wave * 4 + k;
+            const int64_t row = (rb0 + t) * 32 + 2 * j + (lane >> 5);
+            const int64_t o = (row * cols + c0) * 2 + (lane & 31) * 16;
+            dma16_to_lds(rx, (uint8_t*)tile[t] + j * 1024, o < nbytes ? (uint32_t)o : 0x80000000u);
+        }
+    }
+    const int64_t col = c0 + tid;
+    uint32_t wd[kTileBlocks][4];
+    uint32_t sword = 0;
+#pragma unroll
+    for (int t = 0; t < kTileBlocks; ++t) {
+        if (t >= nt) break;
+        // this wave's DMA of tiles 0..t has landed (4 instructions per tile,
+        // issued in order); the barrier publishes every wave's part
+        if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
+        else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+        else if (t == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float a[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) a[r] = __uint_as_float((uint32_t)tile[t][r * kTileCols + tid] << 16);
+        if constexpr (HADN != 0) {
+#pragma unroll
+            for (int r = 0; r < 32; ++r) a[r] = flip_if(a[r], (sign_word >> (r % HADN)) & 1u);
+#pragma unroll
+            for (int o = 0; o < 32; o += HADN) butterflies<HADN>(a + o);
+        }
+        uint32_t m = max_abs_bits<32>(a);
+        if constexpr (HADN != 0) {
+            m = __float_as_uint(__uint_as_float(m) * norm) & 0x7FFFFFFFu;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) a[r] = a[r] * norm;
+        }
+        const uint32_t byte = e8m0_from_amax_bits(m);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wd[t][k] = 0;
+        if (byte != 255u) {
+            if (!SR && byte != 0u) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) wd[t][k] = encode8_hw(a + 8 * k, byte);
+            } else {
+                const uint64_t gbase = ((uint64_t)col * (uint64_t)rows + (uint64_t)(rb0 + t) * 32) >> 2;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+                    if constexpr (SR) {
+                        u0 = stream4(sr_seed, 0u, gbase + 2 * k);
+                        u1 = stream4(sr_seed, 0u, gbase + 2 * k + 1);
+                    }
+                    wd[t][k] = encode8_sw<SR>(a + 8 * k, byte, u0, u1);
+                }
+            }
+        }
+        sword |= byte << (8 * t);
+    }
+    // DMA into tiles past the last row must land before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (col >= cols) return;
+    uint8_t* cdst = codes + col * (rows / 2) + rb0 * 16;
+#pragma unroll
+    for (int t = 0; t < kTileBlocks; ++t) {
+        if (t >= nt) break;
+        *reinterpret_cast<uint4*>(cdst + 16 * t) = make_uint4(wd[t][0], wd[t][1], wd[t][2], wd[t][3]);
+    }
+    uint8_t* sdst = scales + col * nrb + rb0;
+    if (nt == kTileBlocks && (nrb % 4) == 0) {
+        *reinterpret_cast<uint32_t*>(sdst) = sword;
+    } else {
+        for (int t = 0; t < nt; ++t) sdst[t] = (uint8_t)(sword >> (8 * t));
     }
 }
 
@@ -281,6 +420,14 @@ template <int HADN, bool SR>
 hipError_t dispatch_rows_cpl(const void* x, int64_t rows, int64_t cols, uint32_t sign_word,
                              float norm, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
                              hipStream_t st) {
+    if (cols % 8 == 0 && rows * cols * 2 < (INT64_C(1) << 31)) {
+        const int64_t gx = (cols + kTileCols - 1) / kTileCols;
+        const int64_t gy = (rows / 32 + kTileBlocks - 1) / kTileBlocks;
+        hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR>), dim3((unsigned)gx, (unsigned)gy),
+                           dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
+                           sr_seed, codes, scales);
+        return hipGetLastError();
+    }
     if (cols % 4 == 0) return launch_rows<4, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
     if (cols % 2 == 0) return launch_rows<2, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
     return launch_rows<1, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
