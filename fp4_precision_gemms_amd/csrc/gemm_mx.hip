@@ -122,7 +122,7 @@ __device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict_
     return word;
 }
 
-template <int BM, int BN, int BK, int NBUF, int GM, bool KTAIL>
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool KTAIL>
 __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, float* __restrict__ C,
@@ -135,17 +135,23 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int SW = SBY / 4;                    // scale words per row per stage
     constexpr int SRPI = 64 / SW;                  // rows per scale DMA instruction
     constexpr int KS = BK / 64;                    // MFMA k-steps per stage
-    constexpr int FM = BM / 64, FN = BN / 64;      // 32x32 tiles per wave
-    constexpr int LA = BM / RPI / 4, LB = BN / RPI / 4;      // code DMAs per wave per stage
-    constexpr int SLA = BM / SRPI / 4, SLB = BN / SRPI / 4;  // scale DMAs per wave per stage
+    constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA tiles per wave
+    // scale rows are fetched for BM / BN rounded up to whole instructions
+    // over the four waves (the extra rows are never read)
+    constexpr int BMP = (BM + 4 * SRPI - 1) / (4 * SRPI) * (4 * SRPI);
+    constexpr int BNP = (BN + 4 * SRPI - 1) / (4 * SRPI) * (4 * SRPI);
+    constexpr int LA = BM / RPI / 4, LB = BN / RPI / 4;        // code DMAs per wave per stage
+    constexpr int SLA = BMP / SRPI / 4, SLB = BNP / SRPI / 4;  // scale DMAs per wave per stage
     constexpr int DMA_PER_STAGE = LA + LB + (KTAIL ? 0 : SLA + SLB);
     constexpr int kCodesA = 0, kCodesB = BM * RB;
-    constexpr int kScA = (BM + BN) * RB, kScB = kScA + BM * SBY;
-    constexpr int kStage = kScB + BN * SBY;
+    constexpr int kScA = (BM + BN) * RB, kScB = kScA + BMP * SBY;
+    constexpr int kStage = kScB + BNP * SBY;
     constexpr int D = NBUF - 1;                    // stages of DMA in flight
     static_assert(BK == 128 || BK == 256, "stage depth");
     static_assert(NBUF == 2 || NBUF == 4, "stage ring");
-    static_assert(BM % 256 == 0 && BN % 256 == 0, "tile sizes");
+    static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave layout");
+    static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "code DMA split over the waves");
     static_assert(NBUF * kStage <= 160 * 1024, "LDS");
     // Stage buffers as distinct arrays: the compiler can then tell that
     // fragment reads of one do not wait on DMA still landing in another.
@@ -156,264 +162,293 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, l32 = lane & 31;
-    int tile_m, tile_n;
-    tile_of_block<GM>(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tile_m, tile_n);
-    tile_m = __builtin_amdgcn_readfirstlane(tile_m);
-    tile_n = __builtin_amdgcn_readfirstlane(tile_n);
-    const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-    const int64_t kbytes = K / 2, ks = K / 32;
-    const int nk = (int)((K + BK - 1) / BK);
+    const int wm = wave / WN, wn = wave % WN, h = lane >> 5, l32 = lane & 31;
+    // Persistent workgroups: tile t, t + gridDim.x, ... (the grid is at most
+    // one workgroup per CU, so consecutive tile indices still land on the
+    // XCDs round-robin).
+    const int ntiles = tiles_m * tiles_n;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        // every wave is done with the previous tile's LDS before it is refilled
+        if (t != (int)blockIdx.x) {
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+            barrier_after_wait();
+        }
+        int tile_m, tile_n;
+        tile_of_block<GM>(t, ntiles, tiles_m, tiles_n, tile_m, tile_n);
+        tile_m = __builtin_amdgcn_readfirstlane(tile_m);
+        tile_n = __builtin_amdgcn_readfirstlane(tile_n);
+        const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+        const int64_t kbytes = K / 2, ks = K / 32;
+        const int nk = (int)((K + BK - 1) / BK);
 
-    // Buffer views of this block's rows: rows past M / N are out of range.
-    const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
-    const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + m0 * kbytes), (short)0, (int)(rows_a * kbytes), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + n0 * kbytes), (short)0, (int)(rows_b * kbytes), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(SA + m0 * ks), (short)0, (int)(rows_a * ks), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(SB + n0 * ks), (short)0, (int)(rows_b * ks), kBufferWord3);
+        // Buffer views of this block's rows: rows past M / N are out of range.
+        const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
+        const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(A + m0 * kbytes), (short)0, (int)(rows_a * kbytes), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(B + n0 * kbytes), (short)0, (int)(rows_b * kbytes), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(SA + m0 * ks), (short)0, (int)(rows_a * ks), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(SB + n0 * ks), (short)0, (int)(rows_b * ks), kBufferWord3);
 
-    // Per-lane DMA offsets within the stage at k = 0; the stage's k offset
-    // goes in the scalar offset.  Codes: row lane / CPR of an RPI-row group,
-    // the chunk that belongs in slot lane mod CPR of that row.  Scales: row
-    // lane / SW of an SRPI-row group, scale word lane mod SW.
-    const int drow = lane / CPR, dslot = lane % CPR;
-    uint32_t offa[LA], offb[LB], offsa[SLA], offsb[SLB];
-    int chka[LA], chkb[LB];   // byte offset of the fetched chunk within the row
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int row = (wave * LA + i) * RPI + drow;
-        chka[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
-        offa[i] = (uint32_t)(row * kbytes + chka[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int row = (wave * LB + i) * RPI + drow;
-        chkb[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
-        offb[i] = (uint32_t)(row * kbytes + chkb[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < SLA; ++i)
-        offsa[i] = (uint32_t)(((wave * SLA + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
-#pragma unroll
-    for (int i = 0; i < SLB; ++i)
-        offsb[i] = (uint32_t)(((wave * SLB + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
-
-    // A stage kt outside [0, nk) is an all-zero stage (every offset out of
-    // range, zero codes and scale bytes).  Leading zero stages round the
-    // stage count up to a multiple of NBUF for the loop below; trailing ones
-    // are the (unused) prefetches past the last stage, which keep every
-    // stage one straight-line block.
-    auto load_stage = [&](int kt, uint8_t* base) {
-        const bool zero = kt < 0 || kt >= nk;
-        const int kcode = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * RB);
-        // a chunk past the contraction end gets an offset out of range
-        const uint32_t oob = zero ? 0x80000000u : 0u;
-#pragma unroll
+        // Per-lane DMA offsets within the stage at k = 0; the stage's k offset
+        // goes in the scalar offset.  Codes: row lane / CPR of an RPI-row group,
+        // the chunk that belongs in slot lane mod CPR of that row.  Scales: row
+        // lane / SW of an SRPI-row group, scale word lane mod SW.
+        const int drow = lane / CPR, dslot = lane % CPR;
+        uint32_t offa[LA], offb[LB], offsa[SLA], offsb[SLB];
+        int chka[LA], chkb[LB];   // byte offset of the fetched chunk within the row
+    #pragma unroll
         for (int i = 0; i < LA; ++i) {
-            const uint32_t tail = KTAIL ? (uint32_t)(kcode + chka[i] >= kbytes) << 31 : 0u;
-            dma16_to_lds(ra, base + kCodesA + (wave * LA + i) * RPI * RB, offa[i] | oob | tail, kcode);
+            const int row = (wave * LA + i) * RPI + drow;
+            chka[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
+            offa[i] = (uint32_t)(row * kbytes + chka[i]);
         }
-#pragma unroll
+    #pragma unroll
         for (int i = 0; i < LB; ++i) {
-            const uint32_t tail = KTAIL ? (uint32_t)(kcode + chkb[i] >= kbytes) << 31 : 0u;
-            dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * RPI * RB, offb[i] | oob | tail, kcode);
+            const int row = (wave * LB + i) * RPI + drow;
+            chkb[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
+            offb[i] = (uint32_t)(row * kbytes + chkb[i]);
         }
-        if constexpr (!KTAIL) {
-            const int kscale = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * SBY);
-#pragma unroll
-            for (int i = 0; i < SLA; ++i)
-                dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * SRPI * SBY, offsa[i] | oob, kscale);
-#pragma unroll
-            for (int i = 0; i < SLB; ++i)
-                dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, kscale);
-        } else {
-            for (int r = tid; r < BM; r += kThreads) {
-                const int64_t g = m0 + r < M ? m0 + r : M - 1;
-#pragma unroll
-                for (int w = 0; w < SW; ++w)
-                    reinterpret_cast<uint32_t*>(base + kScA + r * SBY)[w] =
-                        zero ? 0u : scale_word_masked<SBY>(SA, g, ks, kt, w);
-            }
-            for (int r = tid; r < BN; r += kThreads) {
-                const int64_t g = n0 + r < N ? n0 + r : N - 1;
-#pragma unroll
-                for (int w = 0; w < SW; ++w)
-                    reinterpret_cast<uint32_t*>(base + kScB + r * SBY)[w] =
-                        zero ? 0u : scale_word_masked<SBY>(SB, g, ks, kt, w);
-            }
-        }
-    };
+    #pragma unroll
+        for (int i = 0; i < SLA; ++i)
+            offsa[i] = (uint32_t)(((wave * SLA + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
+    #pragma unroll
+        for (int i = 0; i < SLB; ++i)
+            offsb[i] = (uint32_t)(((wave * SLB + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
 
-    v16f acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        // A stage kt outside [0, nk) is an all-zero stage (every offset out of
+        // range, zero codes and scale bytes).  Leading zero stages round the
+        // stage count up to a multiple of NBUF for the loop below; trailing ones
+        // are the (unused) prefetches past the last stage, which keep every
+        // stage one straight-line block.
+        auto load_stage = [&](int kt, uint8_t* base) {
+            const bool zero = kt < 0 || kt >= nk;
+            const int kcode = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * RB);
+            // a chunk past the contraction end gets an offset out of range
+            const uint32_t oob = zero ? 0x80000000u : 0u;
+    #pragma unroll
+            for (int i = 0; i < LA; ++i) {
+                const uint32_t tail = KTAIL ? (uint32_t)(kcode + chka[i] >= kbytes) << 31 : 0u;
+                dma16_to_lds(ra, base + kCodesA + (wave * LA + i) * RPI * RB, offa[i] | oob | tail, kcode);
+            }
+    #pragma unroll
+            for (int i = 0; i < LB; ++i) {
+                const uint32_t tail = KTAIL ? (uint32_t)(kcode + chkb[i] >= kbytes) << 31 : 0u;
+                dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * RPI * RB, offb[i] | oob | tail, kcode);
+            }
+            if constexpr (!KTAIL) {
+                const int kscale = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * SBY);
+    #pragma unroll
+                for (int i = 0; i < SLA; ++i)
+                    dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * SRPI * SBY, offsa[i] | oob, kscale);
+    #pragma unroll
+                for (int i = 0; i < SLB; ++i)
+                    dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, kscale);
+            } else {
+                for (int r = tid; r < BM; r += kThreads) {
+                    const int64_t g = m0 + r < M ? m0 + r : M - 1;
+    #pragma unroll
+                    for (int w = 0; w < SW; ++w)
+                        reinterpret_cast<uint32_t*>(base + kScA + r * SBY)[w] =
+                            zero ? 0u : scale_word_masked<SBY>(SA, g, ks, kt, w);
+                }
+                for (int r = tid; r < BN; r += kThreads) {
+                    const int64_t g = n0 + r < N ? n0 + r : N - 1;
+    #pragma unroll
+                    for (int w = 0; w < SW; ++w)
+                        reinterpret_cast<uint32_t*>(base + kScB + r * SBY)[w] =
+                            zero ? 0u : scale_word_masked<SBY>(SB, g, ks, kt, w);
+                }
+            }
+        };
 
-    // Register state: the fragments of two k-steps (k-step s in set s mod 2)
-    // and the scale words of two stages (word w of a fragment row holds the
-    // blocks of k-steps 2w and 2w+1).  Shifted right by 8 h, word s / 2 holds
-    // this lane's block of k-step s in byte 0 (even s) or byte 2 (odd s),
-    // which the MFMA selects by op_sel.
-    struct Scales { uint32_t a[FM][SW], b[FN][SW]; };
-    // native vectors (not HIP's uint4 struct): one 16-byte LDS load each
-    v4i fa[2][FM], fb[2][FN];
-    auto read_frags = [&](const uint8_t* base, int s) {
-        const uint8_t* la = base + kCodesA + wm * (BM / 2) * RB;
-        const uint8_t* lb = base + kCodesB + wn * (BN / 2) * RB;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = i * 32 + l32;
-            fa[s & 1][i] = *reinterpret_cast<const v4i*>(
-                la + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int row = j * 32 + l32;
-            fb[s & 1][j] = *reinterpret_cast<const v4i*>(
-                lb + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
-        }
-    };
-    auto read_scales = [&](const uint8_t* base, Scales& sc) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const uint8_t* p = base + kScA + (wm * (BM / 2) + i * 32 + l32) * SBY;
-#pragma unroll
-            for (int w = 0; w < SW; ++w) sc.a[i][w] = reinterpret_cast<const uint32_t*>(p)[w];
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const uint8_t* p = base + kScB + (wn * (BN / 2) + j * 32 + l32) * SBY;
-#pragma unroll
-            for (int w = 0; w < SW; ++w) sc.b[j][w] = reinterpret_cast<const uint32_t*>(p)[w];
-        }
-    };
-    auto mfmas = [&](int s, const Scales& sc) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const v8i af = __builtin_shufflevector(fa[s & 1][i], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-            const uint32_t wa = sc.a[i][s >> 1] >> (8 * h);
-#pragma unroll
+        v16f acc[FM][FN];
+    #pragma unroll
+        for (int i = 0; i < FM; ++i)
+    #pragma unroll
+            for (int j = 0; j < FN; ++j)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        // Register state: the fragments of two k-steps (k-step s in set s mod 2)
+        // and the scale words of two stages (word w of a fragment row holds the
+        // blocks of k-steps 2w and 2w+1).  Shifted right by 8 h, word s / 2 holds
+        // this lane's block of k-step s in byte 0 (even s) or byte 2 (odd s),
+        // which the MFMA selects by op_sel.
+        struct Scales { uint32_t a[FM][SW], b[FN][SW]; };
+        // native vectors (not HIP's uint4 struct): one 16-byte LDS load each
+        v4i fa[2][FM], fb[2][FN];
+        auto read_frags = [&](const uint8_t* base, int s) {
+            const uint8_t* la = base + kCodesA + wm * TM * RB;
+            const uint8_t* lb = base + kCodesB + wn * TN * RB;
+    #pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = i * 32 + l32;
+                fa[s & 1][i] = *reinterpret_cast<const v4i*>(
+                    la + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
+            }
+    #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const v8i bf = __builtin_shufflevector(fb[s & 1][j], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-                const uint32_t wb = sc.b[j][s >> 1] >> (8 * h);
-                acc[i][j] = (s & 1) ? mfma_fp4_byte2(bf, af, acc[i][j], wb, wa)
-                                    : mfma_fp4_byte0(bf, af, acc[i][j], wb, wa);
+                const int row = j * 32 + l32;
+                fb[s & 1][j] = *reinterpret_cast<const v4i*>(
+                    lb + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
             }
-        }
-    };
+        };
+        auto read_scales = [&](const uint8_t* base, Scales& sc) {
+    #pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const uint8_t* p = base + kScA + (wm * TM + i * 32 + l32) * SBY;
+    #pragma unroll
+                for (int w = 0; w < SW; ++w) sc.a[i][w] = reinterpret_cast<const uint32_t*>(p)[w];
+            }
+    #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const uint8_t* p = base + kScB + (wn * TN + j * 32 + l32) * SBY;
+    #pragma unroll
+                for (int w = 0; w < SW; ++w) sc.b[j][w] = reinterpret_cast<const uint32_t*>(p)[w];
+            }
+        };
+        auto mfmas = [&](int s, const Scales& sc) {
+    #pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const v8i af = __builtin_shufflevector(fa[s & 1][i], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+                const uint32_t wa = sc.a[i][s >> 1] >> (8 * h);
+    #pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const v8i bf = __builtin_shufflevector(fb[s & 1][j], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const uint32_t wb = sc.b[j][s >> 1] >> (8 * h);
+                    acc[i][j] = (s & 1) ? mfma_fp4_byte2(bf, af, acc[i][j], wb, wa)
+                                        : mfma_fp4_byte0(bf, af, acc[i][j], wb, wa);
+                }
+            }
+        };
 
-    // One stage from buffer `cur` (its k-step 0 fragments and scales already
-    // in registers as `sc`); `ahead` receives stage kt + D, `next` holds
-    // stage kt + 1.
-    auto run_stage = [&](const uint8_t* cur, int kt, uint8_t* ahead, const uint8_t* next,
-                         const Scales& sc, Scales& nsc) {
-        load_stage(kt + D, ahead);
-#pragma unroll
-        for (int s = 0; s < KS - 1; ++s) {
-            read_frags(cur, s + 1);
-            mfmas(s, sc);
-        }
-        int dma_left = DMA_PER_STAGE;
-        int ds_left = (KS - 1) * (FM + FN);
-#pragma unroll
-        for (int t = 0; t < (KS - 1) * FM * FN; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-            if (dma_left > 0) {
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
-                --dma_left;
+        // One stage from buffer `cur` (its k-step 0 fragments and scales already
+        // in registers as `sc`); `ahead` receives stage kt + D, `next` holds
+        // stage kt + 1.
+        auto run_stage = [&](const uint8_t* cur, int kt, uint8_t* ahead, const uint8_t* next,
+                             const Scales& sc, Scales& nsc) {
+            load_stage(kt + D, ahead);
+    #pragma unroll
+            for (int s = 0; s < KS - 1; ++s) {
+                read_frags(cur, s + 1);
+                mfmas(s, sc);
             }
-            if ((t & 1) == 0 && ds_left > 0) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                --ds_left;
+            constexpr int kMfma1 = (KS - 1) * FM * FN, kDs1 = (KS - 1) * (FM + FN);
+            int dma_left = DMA_PER_STAGE;
+    #pragma unroll
+            for (int t = 0; t < kMfma1; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                if (dma_left > 0) {
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
+                    --dma_left;
+                }
+                // fragment reads spread evenly over the MFMAs
+                if ((t + 1) * kDs1 / kMfma1 > t * kDs1 / kMfma1)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // this wave's DMA of stage kt + 1 has landed (only the D - 1 younger
-        // stages may still be in flight) and its reads of `cur` are done
+            __builtin_amdgcn_sched_barrier(0);
+            // this wave's DMA of stage kt + 1 has landed (only the D - 1 younger
+            // stages may still be in flight) and its reads of `cur` are done
+            if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+            else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
+            barrier_after_wait();
+            read_scales(next, nsc);
+            read_frags(next, 0);
+            mfmas(KS - 1, sc);
+            constexpr int kMfma2 = FM * FN, kDs2 = (FM + FN) * (1 + SW);
+    #pragma unroll
+            for (int t = 0; t < kMfma2; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+                if ((t + 1) * kDs2 / kMfma2 > t * kDs2 / kMfma2)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                if ((t + 1) * kDs2 / kMfma2 > t * kDs2 / kMfma2 + 1)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
+        const int kfirst = -((NBUF - nk % NBUF) % NBUF);
+    #pragma unroll
+        for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
         if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
         else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
         barrier_after_wait();
-        read_scales(next, nsc);
-        read_frags(next, 0);
-        mfmas(KS - 1, sc);
-#pragma unroll
-        for (int t = 0; t < FM * FN; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+        Scales sc0, sc1;
+        read_scales(bufs[0], sc0);
+        read_frags(bufs[0], 0);
+        for (int kt = kfirst; kt < nk; kt += NBUF) {
+    #pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                if (b & 1)
+                    run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc1, sc0);
+                else
+                    run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc0, sc1);
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);
-    };
 
-    uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
-    const int kfirst = -((NBUF - nk % NBUF) % NBUF);
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
-    if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
-    barrier_after_wait();
-    Scales sc0, sc1;
-    read_scales(bufs[0], sc0);
-    read_frags(bufs[0], 0);
-    for (int kt = kfirst; kt < nk; kt += NBUF) {
-#pragma unroll
-        for (int b = 0; b < NBUF; ++b) {
-            if (b & 1)
-                run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc1, sc0);
-            else
-                run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc0, sc1);
-        }
-    }
+        // the prefetches past the last stage must land before the workgroup
+        // (and its LDS) goes away
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
-    // the prefetches past the last stage must land before the workgroup
-    // (and its LDS) goes away
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-
-    // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
-    // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.
-    const bool vec_store = (N % 4) == 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * (BM / 2) + i * 32 + l32;
-        if (m >= M) continue;
-        float* crow = C + m * N;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * (BN / 2) + j * 32 + 8 * q + 4 * h;
-                const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                             acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                if (vec_store && n + 4 <= N) {
-                    *reinterpret_cast<float4*>(crow + n) = v;
-                } else {
-                    if (n < N) crow[n] = v.x;
-                    if (n + 1 < N) crow[n + 1] = v.y;
-                    if (n + 2 < N) crow[n + 2] = v.z;
-                    if (n + 3 < N) crow[n + 3] = v.w;
+        // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
+        // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.
+        const bool vec_store = (N % 4) == 0;
+    #pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * TM + i * 32 + l32;
+            if (m >= M) continue;
+            float* crow = C + m * N;
+    #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+    #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = n0 + wn * TN + j * 32 + 8 * q + 4 * h;
+                    const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    if (vec_store && n + 4 <= N) {
+                        *reinterpret_cast<float4*>(crow + n) = v;
+                    } else {
+                        if (n < N) crow[n] = v.x;
+                        if (n + 1 < N) crow[n + 1] = v.y;
+                        if (n + 2 < N) crow[n + 2] = v.z;
+                        if (n + 3 < N) crow[n + 3] = v.w;
+                    }
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int NBUF, int GM>
+// Compute units of the current device (queried once per device).
+int cu_count() {
+    static int counts[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (counts[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        counts[dev] = n;
+    }
+    return counts[dev];
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM>
 hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
                         const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
                         hipStream_t st) {
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+    const int64_t grid = tm * tn < cu_count() ? tm * tn : cu_count();
     if (K % BK == 0) {
-        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, BK, NBUF, GM, false>), dim3((unsigned)(tm * tn)),
+        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, false>), dim3((unsigned)grid),
                            dim3(kThreads), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
     } else {
-        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, BK, NBUF, GM, true>), dim3((unsigned)(tm * tn)),
+        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, true>), dim3((unsigned)grid),
                            dim3(kThreads), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
     }
     return hipGetLastError();
@@ -424,11 +459,21 @@ hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
                           hipStream_t st) {
-#ifndef FP4_GEMM_BK
-#define FP4_GEMM_BK 256
-#define FP4_GEMM_NBUF 2
-#endif
-    return launch_tiles<256, 256, FP4_GEMM_BK, FP4_GEMM_NBUF, 8>(aq, as, bq, bs, M, N, K, c, st);
+    // Tile shape: the persistent grid runs ceil(tiles / CUs) rounds of one
+    // tile per CU, each costing about the tile's area, so pick the shape with
+    // the least rounds x area (256 x 256 unless a 224-row or -column tile
+    // removes a partly idle last round, e.g. M = 14336 = 64 x 224).
+    const int64_t cus = cu_count();
+    auto cost = [&](int64_t bm, int64_t bn) {
+        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+        return ((tiles + cus - 1) / cus) * bm * bn;
+    };
+    const int64_t c256 = cost(256, 256), cm = cost(224, 256), cn = cost(256, 224);
+    if (cm < c256 && cm <= cn)
+        return launch_tiles<224, 256, 1, 4, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, st);
+    if (cn < c256)
+        return launch_tiles<256, 224, 4, 1, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, st);
+    return launch_tiles<256, 256, 2, 2, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, st);
 }
 
 }  // namespace fp4dev

@@ -124,3 +124,30 @@ def test_gemm_full_size_sampled(wname):
         ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
         gemm_check(got[mi, ni], ref, mag, TOL)
         assert np.isfinite(got).all()
+
+
+# Shapes on which the tile-shape choice (least rounds x tile area on 256 CUs)
+# takes each of the kernel's tile shapes: 256 x 256 (4096 x 4096), 224 x 256
+# (14336 x 4096, the Wgrad gate/up output) and 256 x 224 (4096 x 14336), with
+# ragged edges and contraction sizes with and without a partial last stage.
+TILE_SHAPES = [(4096, 4096, 512), (4000, 4090, 288), (14336, 4096, 256), (14300, 4000, 320),
+               (4096, 14336, 256), (4090, 14300, 96)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE_SHAPES)
+def test_gemm_tile_shapes_sampled(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    aq, as_ = rand_operands(rng, M, K)
+    bq, bs = rand_operands(rng, N, K)
+    say("gemm tile shapes", M, N, K)
+    got = run(F.fp4_gemm_fprop, (aq, as_, bq, bs), (M, N))
+    # corners, every tile edge of both tilings along a diagonal band, random
+    edges = sorted({0, M - 1} | {e for t in (224, 256) for k in range(1, M // t + 1)
+                                  for e in (k * t - 1, k * t) if e < M})
+    mi = np.concatenate([edges, rng.integers(0, M, 2000)])
+    ni = np.concatenate([[(e * 7919) % N for e in edges], rng.integers(0, N, 2000)])
+    mi = np.concatenate([mi, [0, M - 1, 0, M - 1]])
+    ni = np.concatenate([ni, [0, 0, N - 1, N - 1]])
+    ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
+    gemm_check(got[mi, ni], ref, mag, TOL)
+    assert np.isfinite(got).all()
