@@ -109,10 +109,12 @@ def main() -> int:
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     dY, X = up(dY_np), up(X_np)
-    dytq = torch.empty((N, T // 2), dtype=torch.uint8, device=dev)
-    dyts = torch.empty((N, T // 32), dtype=torch.uint8, device=dev)
-    xtq = torch.empty((K, T // 2), dtype=torch.uint8, device=dev)
-    xts = torch.empty((K, T // 32), dtype=torch.uint8, device=dev)
+    (cq, cs) = F.mx_shapes(T, N, F.AXIS_ROWS)
+    dytq = torch.empty(cq, dtype=torch.uint8, device=dev)
+    dyts = torch.empty(cs, dtype=torch.uint8, device=dev)
+    (cq, cs) = F.mx_shapes(T, K, F.AXIS_ROWS)
+    xtq = torch.empty(cq, dtype=torch.uint8, device=dev)
+    xts = torch.empty(cs, dtype=torch.uint8, device=dev)
     dw = torch.empty((N, K), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 

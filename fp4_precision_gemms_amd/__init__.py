@@ -89,9 +89,11 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
 
 
 def mx_shapes(rows: int, cols: int, axis: int):
-    """(codes shape, scales shape) of fp4_hadamard_quantize's outputs."""
+    """(codes shape, scales shape) of fp4_hadamard_quantize's outputs: codes
+    [R, C/2]; scales k-grouped, [ceil(C/256), R, 8] (block b of row r at
+    [b // 8, r, b % 8])."""
     R, C = (rows, cols) if axis == AXIS_COLS else (cols, rows)
-    return (R, C // 2), (R, C // 32)
+    return (R, C // 2), ((C // 32 + 7) // 8, R, 8)
 
 
 def fp4_hadamard_quantize(x: torch.Tensor, axis: int = AXIS_COLS, had_n: int = 32,
@@ -130,10 +132,15 @@ def _gemm(fn, aq, as_, bq, bs, T, N, K, out_shape, out, stream):
     return out
 
 
+def _sshape(R: int, C: int):
+    """k-grouped scale shape of R rows of C contraction elements."""
+    return ((C // 32 + 7) // 8, R, 8)
+
+
 def fp4_gemm_fprop(xq, xs, wq, ws, out=None, stream=None):
     """y[T, N] = X W^T from xq [T, K/2] and wq [N, K/2] (both blocked along K)."""
     T, K, N = xq.shape[0], xq.shape[1] * 2, wq.shape[0]
-    if wq.shape[1] * 2 != K or xs.shape != (T, K // 32) or ws.shape != (N, K // 32):
+    if wq.shape[1] * 2 != K or tuple(xs.shape) != _sshape(T, K) or tuple(ws.shape) != _sshape(N, K):
         raise ValueError("fprop operand shapes disagree")
     return _gemm(lib().fp4_gemm_fprop, xq, xs, wq, ws, T, N, K, (T, N), out, stream)
 
@@ -141,7 +148,7 @@ def fp4_gemm_fprop(xq, xs, wq, ws, out=None, stream=None):
 def fp4_gemm_dgrad(dyq, dys, wtq, wts, out=None, stream=None):
     """dx[T, K] = dY W from dyq [T, N/2] (blocked along N) and wtq [K, N/2]."""
     T, N, K = dyq.shape[0], dyq.shape[1] * 2, wtq.shape[0]
-    if wtq.shape[1] * 2 != N or dys.shape != (T, N // 32) or wts.shape != (K, N // 32):
+    if wtq.shape[1] * 2 != N or tuple(dys.shape) != _sshape(T, N) or tuple(wts.shape) != _sshape(K, N):
         raise ValueError("dgrad operand shapes disagree")
     return _gemm(lib().fp4_gemm_dgrad, dyq, dys, wtq, wts, T, N, K, (T, K), out, stream)
 
@@ -149,7 +156,7 @@ def fp4_gemm_dgrad(dyq, dys, wtq, wts, out=None, stream=None):
 def fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=None, stream=None):
     """dw[N, K] = dY^T X from dytq [N, T/2] and xtq [K, T/2] (blocked along T)."""
     N, T, K = dytq.shape[0], dytq.shape[1] * 2, xtq.shape[0]
-    if xtq.shape[1] * 2 != T or dyts.shape != (N, T // 32) or xts.shape != (K, T // 32):
+    if xtq.shape[1] * 2 != T or tuple(dyts.shape) != _sshape(N, T) or tuple(xts.shape) != _sshape(K, T):
         raise ValueError("wgrad operand shapes disagree")
     return _gemm(lib().fp4_gemm_wgrad, dytq, dyts, xtq, xts, T, N, K, (N, K), out, stream)
 

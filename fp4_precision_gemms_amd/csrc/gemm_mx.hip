@@ -6,7 +6,10 @@
 // run in MXFP4 on native FP4 matrix cores.  All three are one "TN" product
 //     C[m, n] = sum_k a[m, k] b[n, k]
 // of two operands stored along their contraction axis as E2M1 codes (two per
-// byte, even k in the low nibble) with one E8M0 scale per 32 k.
+// byte, even k in the low nibble) with one E8M0 scale per 32 k.  The scales
+// of an operand with R rows are k-grouped: the 8 bytes of blocks 8g .. 8g+7
+// of row r sit at (g R + r) * 8, so the scales of one 256-k stage of
+// consecutive rows are one contiguous run.
 //
 // Kernel layout (256 threads = 4 waves as 2 x 2, block tile BM x BN, wave
 // tile BM/2 x BN/2 made of 32 x 32 MFMA tiles):
@@ -17,15 +20,15 @@
 //     block's E8M0 scale.  The B tile is passed as the instruction's first
 //     operand, so the accumulator holds C^T: lane l owns row m = l mod 32 of
 //     C and four runs of four consecutive n, each stored as one 16-byte write.
-//   - A stage is BK k: BK/2 code bytes and BK/32 scale bytes per row.  Both
-//     go global -> LDS by buffer_load ... lds (no VGPR round trip) into a
+//   - A stage is BK = 256 k: 128 code bytes and one 8-byte scale group per
+//     row.  Both go global -> LDS by buffer_load ... lds (no VGPR round trip) into a
 //     ring of NBUF stage buffers, NBUF - 1 stages ahead of the MFMAs.  One
 //     dwordx4 instruction fills 64 16-byte slots of consecutive rows, lane i
 //     writing slot i; the lane fetches the chunk that belongs in that slot.
 //     Chunk c of row r sits in slot c XOR ((r / (16 / CPR)) mod CPR), CPR the
 //     chunks per row: the 16 lanes the LDS serves per clock (rows r..r+15 of
-//     one chunk) then hit all 64 banks once.  Dword instructions fill the
-//     scale bytes of 64 / (BK / 128) rows.  Rows past M (or N) lie outside
+//     one chunk) then hit all 64 banks once.  A dword instruction copies the
+//     contiguous scale groups of 32 rows.  Rows past M (or N) lie outside
 //     the buffer range and read as zero.
 //   - Per stage a wave issues the DMA of stage kt + NBUF - 1 and the fragment
 //     reads of its k-steps 1.. between the MFMAs of its k-steps 0.., then
@@ -33,8 +36,8 @@
 //     visible to all waves and frees buffer kt; the scales and k-step 0
 //     fragments of stage kt + 1 are read while the last k-step's MFMAs run.
 //   - A contraction that is not a multiple of BK (KTAIL) zero-fills the
-//     missing code chunks through out-of-range offsets and loads the last
-//     stage's scales through registers with the missing blocks set to 127.
+//     missing code chunks through out-of-range offsets and loads the scales
+//     through registers with the blocks past the end set to 127.
 //   - Block order: workgroups are dispatched round-robin over the 8 XCDs;
 //     the block index is remapped so that each XCD works on a contiguous run
 //     of tiles, ordered in groups of GM tile-rows, so tiles that share A and
@@ -105,20 +108,16 @@ __device__ __forceinline__ void tile_of_block(int b, int nb, int tm, int tn, int
     tile_n = r / gm;
 }
 
-// Scale word w (bytes 4w .. 4w+3) of stage kt of one row, SBY scale bytes
-// per row and stage; blocks at or past ks read as 127 (2^0; their codes are
-// zero), packed little-endian.
-template <int SBY>
-__device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict__ S, int64_t row,
-                                                      int64_t ks, int kt, int w) {
-    const int64_t b0 = (int64_t)kt * SBY + 4 * w;
+// Scale word w (bytes 4w .. 4w+3 of group kt) of one row of an operand with
+// R rows and ks blocks per row, k-grouped; blocks at or past ks (the unused
+// tail of the last group) read as 127 (2^0; their codes are zero).
+__device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict__ S, int64_t R,
+                                                      int64_t row, int64_t ks, int kt, int w) {
+    const int64_t b0 = (int64_t)kt * 8 + 4 * w;
+    const uint8_t* p = S + ((int64_t)kt * R + row) * 8 + 4 * w;
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t c = b0 + i < ks ? b0 + i : ks - 1;
-        const uint32_t v = S[row * ks + c];
-        word |= (b0 + i < ks ? v : 127u) << (8 * i);
-    }
+    for (int i = 0; i < 4; ++i) word |= (b0 + i < ks ? (uint32_t)p[i] : 127u) << (8 * i);
     return word;
 }
 
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int CPR = RB / 16;                   // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                  // rows per code DMA instruction
     constexpr int SWZ = 16 / CPR;                  // rows sharing a swizzle value
-    constexpr int SBY = BK / 32;                   // scale bytes per row per stage
+    constexpr int SBY = BK / 32;                   // scale bytes per row per stage (one group)
     constexpr int SW = SBY / 4;                    // scale words per row per stage
     constexpr int SRPI = 64 / SW;                  // rows per scale DMA instruction
     constexpr int KS = BK / 64;                    // MFMA k-steps per stage
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int kScA = (BM + BN) * RB, kScB = kScA + BMP * SBY;
     constexpr int kStage = kScB + BNP * SBY;
     constexpr int D = NBUF - 1;                    // stages of DMA in flight
-    static_assert(BK == 128 || BK == 256, "stage depth");
+    static_assert(BK == 256, "a stage is one 8-block scale group");
     static_assert(NBUF == 2 || NBUF == 4, "stage ring");
     static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave layout");
     static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "code DMA split over the waves");
@@ -188,15 +187,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
             (void*)(A + m0 * kbytes), (short)0, (int)(rows_a * kbytes), kBufferWord3);
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(B + n0 * kbytes), (short)0, (int)(rows_b * kbytes), kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(SA + m0 * ks), (short)0, (int)(rows_a * ks), kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(SB + n0 * ks), (short)0, (int)(rows_b * ks), kBufferWord3);
 
         // Per-lane DMA offsets within the stage at k = 0; the stage's k offset
         // goes in the scalar offset.  Codes: row lane / CPR of an RPI-row group,
-        // the chunk that belongs in slot lane mod CPR of that row.  Scales: row
-        // lane / SW of an SRPI-row group, scale word lane mod SW.
+        // the chunk that belongs in slot lane mod CPR of that row.  Scales: the
+        // contiguous groups of an SRPI-row run, one word per lane.
         const int drow = lane / CPR, dslot = lane % CPR;
         uint32_t offa[LA], offb[LB], offsa[SLA], offsb[SLB];
         int chka[LA], chkb[LB];   // byte offset of the fetched chunk within the row
@@ -214,10 +209,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         }
     #pragma unroll
         for (int i = 0; i < SLA; ++i)
-            offsa[i] = (uint32_t)(((wave * SLA + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
+            offsa[i] = (uint32_t)(((wave * SLA + i) * SRPI * SBY) + lane * 4);
     #pragma unroll
         for (int i = 0; i < SLB; ++i)
-            offsb[i] = (uint32_t)(((wave * SLB + i) * SRPI + lane / SW) * ks + (lane % SW) * 4);
+            offsb[i] = (uint32_t)(((wave * SLB + i) * SRPI * SBY) + lane * 4);
 
         // A stage kt outside [0, nk) is an all-zero stage (every offset out of
         // range, zero codes and scale bytes).  Leading zero stages round the
@@ -240,27 +235,32 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
                 dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * RPI * RB, offb[i] | oob | tail, kcode);
             }
             if constexpr (!KTAIL) {
-                const int kscale = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * SBY);
+                // group kt of this tile's rows: one contiguous run per operand
+                const int64_t g = zero ? 0 : kt;
+                const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(SA + (g * M + m0) * SBY), (short)0, (int)(rows_a * SBY), kBufferWord3);
+                const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(SB + (g * N + n0) * SBY), (short)0, (int)(rows_b * SBY), kBufferWord3);
     #pragma unroll
                 for (int i = 0; i < SLA; ++i)
-                    dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * SRPI * SBY, offsa[i] | oob, kscale);
+                    dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * SRPI * SBY, offsa[i] | oob, 0);
     #pragma unroll
                 for (int i = 0; i < SLB; ++i)
-                    dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, kscale);
+                    dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, 0);
             } else {
                 for (int r = tid; r < BM; r += kThreads) {
                     const int64_t g = m0 + r < M ? m0 + r : M - 1;
     #pragma unroll
                     for (int w = 0; w < SW; ++w)
                         reinterpret_cast<uint32_t*>(base + kScA + r * SBY)[w] =
-                            zero ? 0u : scale_word_masked<SBY>(SA, g, ks, kt, w);
+                            zero ? 0u : scale_word_masked(SA, M, g, ks, kt, w);
                 }
                 for (int r = tid; r < BN; r += kThreads) {
                     const int64_t g = n0 + r < N ? n0 + r : N - 1;
     #pragma unroll
                     for (int w = 0; w < SW; ++w)
                         reinterpret_cast<uint32_t*>(base + kScB + r * SBY)[w] =
-                            zero ? 0u : scale_word_masked<SBY>(SB, g, ks, kt, w);
+                            zero ? 0u : scale_word_masked(SB, N, g, ks, kt, w);
                 }
             }
         };

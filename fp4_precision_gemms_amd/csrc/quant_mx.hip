@@ -7,7 +7,12 @@
 // нестабильности": a Hadamard transform, deterministic or after random sign
 // flips, applied before quantization.
 //
-// Two kernels, one per block axis:
+// Scales are written k-grouped, the layout the GEMM stages load in one
+// contiguous run: for an output of R rows (the logical rows of x or x^T) and
+// nb blocks per row, block b of row r goes to byte ((b / 8) R + r) * 8 +
+// b mod 8.  Bytes of the last group past nb are not written.
+//
+// Kernels, by block axis:
 //   quant_mx_along_cols -- blocks run along the contiguous dim.  A lane owns 8
 //     consecutive elements (one 16-byte load); four adjacent lanes own a
 //     block.  The first three butterfly stages are in registers, the strides
@@ -105,7 +110,8 @@ constexpr int kColsUnroll = 4;
 template <int HADN, bool SR>
 __global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
     const uint4* __restrict__ x, int64_t nchunks, uint32_t sign_word, float norm,
-    uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t nb,
+    int64_t nrows, double inv_nb) {
     uint4 w[kColsUnroll];
     int64_t g[kColsUnroll];
 #pragma unroll
@@ -161,7 +167,16 @@ __global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
             }
         }
         codes[g[u]] = word;
-        if (q == 0) scales[g[u] >> 2] = (uint8_t)byte;
+        if (q == 0) {
+            // block (r, b) of the flat block index; the double quotient is
+            // off by at most one for any index below 2^52
+            const int64_t blk = g[u] >> 2;
+            int64_t r = (int64_t)((double)blk * inv_nb);
+            if (r * nb > blk) --r;
+            if ((r + 1) * nb <= blk) ++r;
+            const int64_t b = blk - r * nb;
+            scales[((b >> 3) * nrows + r) * 8 + (b & 7)] = (uint8_t)byte;
+        }
     }
 }
 
@@ -257,12 +272,12 @@ __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
             sword[c] |= byte << (8 * i);
         }
     }
-    // scale bytes rb0 .. rb0+3 of each column: one aligned word when all four
-    // blocks exist and the row of scales is a multiple of 4 bytes
-    const bool word_ok = rb0 + RBW <= nrb && (nrb % 4) == 0;
+    // scale bytes rb0 .. rb0+3 of each column (half of a k-group, rb0 a
+    // multiple of 4): one aligned word when all four blocks exist
+    const bool word_ok = rb0 + RBW <= nrb;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-        uint8_t* dst = scales + (col0 + c) * nrb + rb0;
+        uint8_t* dst = scales + ((rb0 >> 3) * cols + col0 + c) * 8 + (rb0 & 7);
         if (word_ok) {
             *reinterpret_cast<uint32_t*>(dst) = sword[c];
         } else {
@@ -383,8 +398,9 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
         if (t >= nt) break;
         *reinterpret_cast<uint4*>(cdst + 16 * t) = make_uint4(wd[t][0], wd[t][1], wd[t][2], wd[t][3]);
     }
-    uint8_t* sdst = scales + col * nrb + rb0;
-    if (nt == kTileBlocks && (nrb % 4) == 0) {
+    // rb0 is a multiple of 4: blocks rb0 .. rb0+3 are one half of a k-group
+    uint8_t* sdst = scales + ((rb0 >> 3) * cols + col) * 8 + (rb0 & 7);
+    if (nt == kTileBlocks) {
         *reinterpret_cast<uint32_t*>(sdst) = sword;
     } else {
         for (int t = 0; t < nt; ++t) sdst[t] = (uint8_t)(sword >> (8 * t));
@@ -399,7 +415,7 @@ hipError_t launch_cols(const void* x, int64_t rows, int64_t cols, uint32_t sign_
     const int64_t blocks = (nchunks + per_block - 1) / per_block;
     hipLaunchKernelGGL((quant_mx_along_cols<HADN, SR>), dim3((unsigned)blocks), dim3(kColsThreads),
                        0, st, (const uint4*)x, nchunks, sign_word, norm, sr_seed,
-                       (uint32_t*)codes, scales);
+                       (uint32_t*)codes, scales, cols / 32, rows, 1.0 / (double)(cols / 32));
     return hipGetLastError();
 }
 

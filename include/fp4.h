@@ -64,10 +64,21 @@ typedef enum {
  * contraction axis of that operand). */
 typedef enum {
     FP4_AXIS_COLS = 0,   /* blocks along cols (contiguous): codes [rows, cols/2],
-                            scales [rows, cols/32]                              */
+                            rows x cols/32 scales                               */
     FP4_AXIS_ROWS = 1    /* blocks along rows (strided), i.e. quantize x^T:
-                            codes [cols, rows/2], scales [cols, rows/32]        */
+                            codes [cols, rows/2], cols x rows/32 scales         */
 } fp4_axis;
+
+/* MXFP4 scale layout ("k-grouped"), used by every MXFP4 entry point.  The
+ * E8M0 scales of an operand with R logical rows and nb = C/32 blocks per row
+ * are stored in groups of 8 consecutive blocks: the byte of block b of row r
+ * is at offset ((b / 8) * R + r) * 8 + b % 8, i.e. an array [ceil(nb/8)][R][8]
+ * of FP4_SCALE_BYTES(R, C) bytes.  One group is the 256-element contraction
+ * slice a GEMM stage consumes, so a stage's scales for consecutive rows are
+ * one contiguous run.  When nb % 8 != 0 the last group's bytes past block
+ * nb - 1 are padding: the quantizer does not write them and the GEMMs ignore
+ * them. */
+#define FP4_SCALE_BYTES(R, C) ((((int64_t)(C) / 32 + 7) / 8) * (int64_t)(R) * 8)
 
 /* Block rotation applied before quantization, along the block axis.
  * [AMD-MXFP4, "Поисковая экспериментальная работа..."]: a Hadamard transform,
@@ -103,8 +114,9 @@ typedef enum {
  *      Philox4x32-10(key = sr_seed, counter = (idx >> 2, 0, 0) as 32-bit words
  *      (lo, hi, 0, 0)), idx = r * C + c the element's position in [R, C].
  *   4. codes: two per byte, the even element in the low nibble.
- * Output layout: codes [R, C/2], scales [R, C/32] with (R, C) = (rows, cols)
- * for AXIS_COLS and (cols, rows) for AXIS_ROWS.
+ * Output layout: codes [R, C/2] and the k-grouped scales of R rows of C/32
+ * blocks (FP4_SCALE_BYTES(R, C) bytes), with (R, C) = (rows, cols) for
+ * AXIS_COLS and (cols, rows) for AXIS_ROWS.
  * Requirements: C % 32 == 0; x, codes, scales 16-byte aligned.
  * had_n is ignored when had == FP4_HAD_NONE; sign_seed is ignored unless
  * SIGNED; sr_seed is ignored unless rnd == FP4_SR.  For Wgrad, quantize dY
@@ -123,7 +135,8 @@ fp4_status fp4_hadamard_quantize(const void* x_bf16, int64_t rows, int64_t cols,
  * cores.  Each computes, in fp32 accumulation,
  *     C[m, n] = sum_k  e2m1(a[m,k]) 2^(sa[m,k/32]-127) * e2m1(b[n,k]) 2^(sb[n,k/32]-127)
  * over two MXFP4 operands stored along their contraction axis (codes [rows,
- * Kc/2], scales [rows, Kc/32], as fp4_hadamard_quantize writes them).  C is
+ * Kc/2] and k-grouped scales of rows x Kc/32 blocks, as fp4_hadamard_quantize
+ * writes them).  C is
  * written (overwritten, not accumulated) as row-major fp32.
  * Requirements: T, N, K > 0; the contraction size a multiple of 32 and
  * below 2^24; at most 2^24 - 1 output tiles of 256 x 256; all pointers

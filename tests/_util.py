@@ -33,6 +33,24 @@ def say(*args):
     print("[case]", *args, flush=True)
 
 
+def group_scales(s: np.ndarray, pad: int = 0xFF) -> np.ndarray:
+    """Row-major E8M0 scales [R, nb] -> the library's k-grouped layout
+    [ceil(nb/8), R, 8] (block b of row r at [b // 8, r, b % 8]).  The unused
+    tail of the last group gets `pad` (0xFF, a NaN scale, by default: a GEMM
+    that read it would show NaN)."""
+    R, nb = s.shape
+    G = (nb + 7) // 8
+    p = np.full((R, G * 8), pad, dtype=np.uint8)
+    p[:, :nb] = s
+    return np.ascontiguousarray(p.reshape(R, G, 8).transpose(1, 0, 2))
+
+
+def ungroup_scales(g: np.ndarray, nb: int) -> np.ndarray:
+    """k-grouped scales [G, R, 8] -> row-major [R, nb] (drops the tail)."""
+    G, R, _ = g.shape
+    return np.ascontiguousarray(g.transpose(1, 0, 2).reshape(R, G * 8)[:, :nb])
+
+
 def sentinel_u8(shape) -> torch.Tensor:
     return torch.full(shape, 0xCD, dtype=torch.uint8, device="cuda")
 

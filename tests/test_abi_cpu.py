@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import fp4_precision_gemms_amd as F
@@ -131,3 +132,23 @@ def test_binding_refuses_cpu_tensors():
         pytest.skip("libfp4.so not built")
     with pytest.raises((ValueError, TypeError)):
         F.fp4_hadamard_quantize(torch.zeros(32, 32, dtype=torch.bfloat16))
+
+
+def test_grouped_scale_layout_helpers():
+    """The k-grouped MXFP4 scale layout of include/fp4.h: block b of row r at
+    byte ((b // 8) * R + r) * 8 + b % 8 of a [ceil(nb/8), R, 8] array."""
+    from _util import group_scales, ungroup_scales
+    rng = np.random.default_rng(3)
+    R, nb = 37, 13
+    s = rng.integers(0, 255, (R, nb), dtype=np.uint8)
+    g = group_scales(s)
+    assert g.shape == (2, R, 8)
+    flat = g.reshape(-1)
+    for r in range(R):
+        for b in range(nb):
+            assert flat[((b // 8) * R + r) * 8 + b % 8] == s[r, b]
+    assert (g[1, :, nb - 8:] == 0xFF).all()
+    assert np.array_equal(ungroup_scales(g, nb), s)
+    assert F.mx_shapes(64, 416, F.AXIS_COLS) == ((64, 208), (2, 64, 8))
+    assert F.mx_shapes(416, 64, F.AXIS_ROWS) == ((64, 208), (2, 64, 8))
+    assert F.mx_shapes(3, 256, F.AXIS_COLS)[1] == (1, 3, 8)

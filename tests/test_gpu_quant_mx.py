@@ -9,7 +9,7 @@ import torch
 import fp4_precision_gemms_amd as F
 import oracle as O
 import workloads as W
-from _util import bf16_bits, need_gpu, say, sentinel_u8, to_gpu_bf16
+from _util import bf16_bits, need_gpu, say, sentinel_u8, to_gpu_bf16, ungroup_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,12 @@ def gpu_quant(bits, axis, had, had_n, rnd, sign_seed=0, sr_seed=0):
     codes, scales = sentinel_u8(cs), sentinel_u8(ss)
     F.fp4_hadamard_quantize(x, AX[axis], had_n, HD[had], sign_seed, RN[rnd], sr_seed, codes, scales)
     torch.cuda.synchronize()
-    return codes.cpu().numpy(), scales.cpu().numpy()
+    g = scales.cpu().numpy()
+    nb = (cols if axis == O.AXIS_COLS else rows) // 32
+    # the padding of the last k-group is never written
+    tail = g[-1, :, nb - 8 * (g.shape[0] - 1):]
+    assert (tail == 0xCD).all(), "quantizer wrote the scale padding"
+    return codes.cpu().numpy(), ungroup_scales(g, nb)
 
 
 def assert_same(got, ref, what):
