@@ -8,6 +8,8 @@ then dW[N, K] = dY^T X on the scaled FP4 matrix cores, fp32 output.  Inputs
 are synthetic bf16 tensors resident in HBM before timing starts.
 
     python bench.py [--steps K] [--warmup W] [--workload gate_up] [--no-cpu-baseline]
+                    [--copy-calibration]
+    python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
 (2 T N K flops over the whole step); the roofline object describes the
@@ -53,6 +55,75 @@ def traffic_per_launch():
     return None
 
 
+COPY_BYTES = 256 << 20           # the calibration copy reads and writes this many bytes
+
+
+def copy_calibration(torch, dev):
+    """A plain elementwise copy of known size (float32 negation, 256 MiB read
+    and 256 MiB written), launched a few times so that a counter run over
+    this program sees it next to the GEMM: its FETCH_SIZE / WRITE_SIZE
+    readings give the bytes-per-count factors of the two counters."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize(dev)
+
+
+def counter_summary(fetch_dir, write_dir):
+    """Reads the rocprofv3 counter CSVs of two runs of
+        rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run --
+            python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
+    and writes the calibrated HBM traffic per GEMM launch next to the kernel
+    trace summaries (JSON for bench.py, Markdown for readers)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter CSV under %s" % d)
+        disp = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], f, r["Dispatch_Id"])
+                disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (k, _, _), v in disp.items():
+            out.setdefault(k, []).append(v)
+        return out
+
+    def pick(table, needle):
+        hits = {k: v for k, v in table.items() if needle in k}
+        if len(hits) != 1:
+            raise SystemExit("expected one kernel matching %r, found %s" % (needle, list(hits)))
+        (name, vals), = hits.items()
+        return name, sum(vals) / len(vals), len(vals)
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    gname, g_fetch, nf = pick(fetch, "gemm_mx_tn")
+    _, g_write, nw = pick(write, "gemm_mx_tn")
+    cname, c_fetch, _ = pick(fetch, "neg")
+    _, c_write, _ = pick(write, "neg")
+    f_fetch = COPY_BYTES / (c_fetch * 1024.0)        # counters are in KiB
+    f_write = COPY_BYTES / (c_write * 1024.0)
+    rd, wr = g_fetch * 1024.0 * f_fetch, g_write * 1024.0 * f_write
+    rec = {"kernel": gname, "dispatches": [nf, nw],
+           "gemm_fetch_kib": g_fetch, "gemm_write_kib": g_write,
+           "copy_kernel": cname, "copy_bytes_each_way": COPY_BYTES,
+           "copy_fetch_kib": c_fetch, "copy_write_kib": c_write,
+           "fetch_factor": f_fetch, "write_factor": f_write,
+           "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+           "hbm_bytes_per_launch": rd + wr,
+           "gemm_source_sha256": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()}
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
 def cpu_baseline(w, dY, X):
     """The oracle, untuned, on a bounded sample of the same Wgrad: the full
     Hadamard-32 + MXFP4 quantization of dY and X along tokens, then 256 of
@@ -84,7 +155,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gate_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (counter calibration)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 counter runs and exit")
     args = ap.parse_args()
+    if args.counters:
+        return counter_summary(*args.counters)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -174,6 +251,8 @@ def main() -> int:
                       "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
                       "gemm_TFLOPs": gemm_tflops},
     }
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, dY_np, X_np)
     print(json.dumps(out), flush=True)
