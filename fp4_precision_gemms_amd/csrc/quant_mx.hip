@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
         }
     }
     const int64_t col = c0 + tid;
-    uint32_t wd[kTileBlocks][4];
+    uint32_t wd[kTileBlocks][4] = {};
     uint32_t sword = 0;
 #pragma unroll
     for (int t = 0; t < kTileBlocks; ++t) {
@@ -389,15 +389,31 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
         }
         sword |= byte << (8 * t);
     }
-    // DMA into tiles past the last row must land before the workgroup ends
+    // DMA into tiles past the last row must land before the tiles are reused
+    // (and before the workgroup ends)
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (col >= cols) return;
-    uint8_t* cdst = codes + col * (rows / 2) + rb0 * 16;
+    // Codes leave through LDS: thread c's 64 bytes go to row c of a
+    // [256][80-byte] staging array (the 16-byte pad makes both the row writes
+    // and the chunk reads below conflict-free), then each wave stores 16
+    // columns x 64 bytes per instruction (4 lanes per column) instead of 64
+    // columns x 16 bytes.  The staging array (20 KB) overlays the tiles.
+    __syncthreads();                                   // every tile has been read
+    constexpr int kStageRow = 80;
+    static_assert(kTileCols * kStageRow <= (int)sizeof(tile), "staging fits the tiles");
+    uint8_t* stg = reinterpret_cast<uint8_t*>(&tile[0][0]);
 #pragma unroll
-    for (int t = 0; t < kTileBlocks; ++t) {
-        if (t >= nt) break;
-        *reinterpret_cast<uint4*>(cdst + 16 * t) = make_uint4(wd[t][0], wd[t][1], wd[t][2], wd[t][3]);
+    for (int t = 0; t < kTileBlocks; ++t)
+        *reinterpret_cast<uint4*>(stg + tid * kStageRow + 16 * t) =
+            make_uint4(wd[t][0], wd[t][1], wd[t][2], wd[t][3]);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = wave * 64 + i * 16 + (lane >> 2), chunk = lane & 3;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + c * kStageRow + 16 * chunk);
+        if (chunk < nt && c0 + c < cols)
+            *reinterpret_cast<uint4*>(codes + (c0 + c) * (rows / 2) + (rb0 + chunk) * 16) = v;
     }
+    if (col >= cols) return;
     // rb0 is a multiple of 4: blocks rb0 .. rb0+3 are one half of a k-group
     uint8_t* sdst = scales + ((rb0 >> 3) * cols + col) * 8 + (rb0 & 7);
     if (nt == kTileBlocks) {
