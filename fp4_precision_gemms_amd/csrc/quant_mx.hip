@@ -18,8 +18,13 @@
 //     block.  The first three butterfly stages are in registers, the strides
 //     8 and 16 cross lanes through DPP quad permutes, the block maximum is a
 //     two-step DPP reduction, and each lane stores its 8 codes as one dword.
-//   quant_mx_along_rows -- blocks run along the strided dim (x^T is
-//     quantized, as Wgrad needs: blocks along tokens).  A lane owns CPL
+//   quant_mx_along_rows_lds -- blocks run along the strided dim (x^T is
+//     quantized, as Wgrad needs: blocks along tokens).  32 x 256 bf16 tiles
+//     go global -> LDS by DMA, one thread per column transposes through LDS,
+//     and the codes leave through an LDS staging array in column-major
+//     store instructions.  Used whenever cols % 8 == 0 and the input is
+//     below 2 GiB.
+//   quant_mx_along_rows -- the same axis, any column count: a lane owns CPL
 //     adjacent columns and RBW consecutive 32-row blocks of each: per block
 //     it issues 32 row loads (adjacent lanes read adjacent columns, so every
 //     load instruction reads one contiguous 64*CPL*2-byte row segment), then
@@ -296,21 +301,44 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* 
 }
 
 constexpr int kTileCols = 256;           // columns per block, one per thread
-constexpr int kTileBlocks = 4;           // 32-row blocks per workgroup
-constexpr int kTileBytes = 32 * kTileCols * 2;
+
+// s_waitcnt vmcnt(N) (N <= 63), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Waits until at most 4 (TB - 1 - t) DMA instructions are outstanding: the
+// four of tile t and all before it have landed (t < TB <= 8).
+template <int TB>
+__device__ __forceinline__ void wait_tile(int t) {
+    switch (t) {
+    case 0: wait_vmcnt<(TB > 0 ? 4 * (TB - 1) : 0)>(); break;
+    case 1: wait_vmcnt<(TB > 1 ? 4 * (TB - 2) : 0)>(); break;
+    case 2: wait_vmcnt<(TB > 2 ? 4 * (TB - 3) : 0)>(); break;
+    case 3: wait_vmcnt<(TB > 3 ? 4 * (TB - 4) : 0)>(); break;
+    case 4: wait_vmcnt<(TB > 4 ? 4 * (TB - 5) : 0)>(); break;
+    case 5: wait_vmcnt<(TB > 5 ? 4 * (TB - 6) : 0)>(); break;
+    case 6: wait_vmcnt<(TB > 6 ? 4 * (TB - 7) : 0)>(); break;
+    default: wait_vmcnt<0>(); break;
+    }
+}
 
 // Blocks along rows, staged through LDS: a workgroup owns 256 adjacent
-// columns and 4 consecutive 32-row blocks.  All four 32 x 256 bf16 tiles go
+// columns and TB consecutive 32-row blocks.  All TB 32 x 256 bf16 tiles go
 // global -> LDS by DMA up front (each wave instruction moves two 512-byte
 // row segments); tile t is processed once its DMA has landed.  Thread c
 // owns column c: it reads the column's 32 values of a tile from LDS
 // (consecutive lanes, consecutive columns: conflict-free), transforms and
-// encodes them, and at the end stores its 4 blocks' codes as 64 contiguous
-// bytes and their scales as one 4-byte word.  Needs cols % 8 == 0.
-template <int HADN, bool SR>
+// encodes them; at the end the TB blocks' codes of a column (16 TB
+// contiguous bytes) leave through LDS in column-major store instructions and
+// the TB scale bytes as one word.  Needs cols % 8 == 0.
+template <int HADN, bool SR, int TB>
 __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
     uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    static_assert(TB == 2 || TB == 4 || TB == 8, "blocks per workgroup");
+    constexpr int kTileBlocks = TB;
     __shared__ __attribute__((aligned(1024))) uint16_t tile[kTileBlocks][32 * kTileCols];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -339,16 +367,13 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
     }
     const int64_t col = c0 + tid;
     uint32_t wd[kTileBlocks][4] = {};
-    uint32_t sword = 0;
+    uint64_t sword = 0;
 #pragma unroll
     for (int t = 0; t < kTileBlocks; ++t) {
         if (t >= nt) break;
         // this wave's DMA of tiles 0..t has landed (4 instructions per tile,
         // issued in order); the barrier publishes every wave's part
-        if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | 12);
-        else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
-        else if (t == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-        else __builtin_amdgcn_s_waitcnt(0x0F70);
+        wait_tile<TB>(t);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -387,18 +412,19 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
                 }
             }
         }
-        sword |= byte << (8 * t);
+        sword |= (uint64_t)byte << (8 * t);
     }
     // DMA into tiles past the last row must land before the tiles are reused
     // (and before the workgroup ends)
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    // Codes leave through LDS: thread c's 64 bytes go to row c of a
-    // [256][80-byte] staging array (the 16-byte pad makes both the row writes
-    // and the chunk reads below conflict-free), then each wave stores 16
-    // columns x 64 bytes per instruction (4 lanes per column) instead of 64
-    // columns x 16 bytes.  The staging array (20 KB) overlays the tiles.
+    // Codes leave through LDS: thread c's 16 TB bytes go to row c of a
+    // [256][16 TB + 16 byte] staging array (the 16-byte pad makes both the
+    // row writes and the chunk reads below conflict-free), then each wave
+    // stores 64 / TB columns x 16 TB bytes per instruction (TB lanes per
+    // column) instead of 64 columns x 16 bytes.  The staging array overlays
+    // the tiles.
     __syncthreads();                                   // every tile has been read
-    constexpr int kStageRow = 80;
+    constexpr int kStageRow = 16 * TB + 16;
     static_assert(kTileCols * kStageRow <= (int)sizeof(tile), "staging fits the tiles");
     uint8_t* stg = reinterpret_cast<uint8_t*>(&tile[0][0]);
 #pragma unroll
@@ -407,17 +433,19 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
             make_uint4(wd[t][0], wd[t][1], wd[t][2], wd[t][3]);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = wave * 64 + i * 16 + (lane >> 2), chunk = lane & 3;
+    for (int i = 0; i < TB; ++i) {
+        const int c = wave * 64 + i * (64 / TB) + lane / TB, chunk = lane % TB;
         const uint4 v = *reinterpret_cast<const uint4*>(stg + c * kStageRow + 16 * chunk);
         if (chunk < nt && c0 + c < cols)
             *reinterpret_cast<uint4*>(codes + (c0 + c) * (rows / 2) + (rb0 + chunk) * 16) = v;
     }
     if (col >= cols) return;
-    // rb0 is a multiple of 4: blocks rb0 .. rb0+3 are one half of a k-group
+    // rb0 is a multiple of TB: blocks rb0 .. rb0+TB-1 lie in one k-group
     uint8_t* sdst = scales + ((rb0 >> 3) * cols + col) * 8 + (rb0 & 7);
     if (nt == kTileBlocks) {
-        *reinterpret_cast<uint32_t*>(sdst) = sword;
+        if constexpr (TB == 2) *reinterpret_cast<uint16_t*>(sdst) = (uint16_t)sword;
+        else if constexpr (TB == 4) *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)sword;
+        else *reinterpret_cast<uint64_t*>(sdst) = sword;
     } else {
         for (int t = 0; t < nt; ++t) sdst[t] = (uint8_t)(sword >> (8 * t));
     }
@@ -448,14 +476,21 @@ hipError_t launch_rows(const void* x, int64_t rows, int64_t cols, uint32_t sign_
     return hipGetLastError();
 }
 
+// 32-row blocks per workgroup of the LDS kernel: two (32 KB of LDS) keeps
+// five workgroups' DMA in flight per CU; measured on dY[8192x14336] and
+// X[8192x4096], two is as fast as four on the large input and 10 % faster on
+// the small one, and eight (one workgroup per CU) is 1.5-1.8x slower.
+constexpr int kRowsLdsBlocks = 2;
+
 template <int HADN, bool SR>
 hipError_t dispatch_rows_cpl(const void* x, int64_t rows, int64_t cols, uint32_t sign_word,
                              float norm, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
                              hipStream_t st) {
     if (cols % 8 == 0 && rows * cols * 2 < (INT64_C(1) << 31)) {
         const int64_t gx = (cols + kTileCols - 1) / kTileCols;
-        const int64_t gy = (rows / 32 + kTileBlocks - 1) / kTileBlocks;
-        hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR>), dim3((unsigned)gx, (unsigned)gy),
+        constexpr int TB = kRowsLdsBlocks;
+        const int64_t gy = (rows / 32 + TB - 1) / TB;
+        hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB>), dim3((unsigned)gx, (unsigned)gy),
                            dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
                            sr_seed, codes, scales);
         return hipGetLastError();
