@@ -11,8 +11,10 @@
 // of row r sit at (g R + r) * 8, so the scales of one 256-k stage of
 // consecutive rows are one contiguous run.
 //
-// Kernel layout (256 threads = 4 waves as 2 x 2, block tile BM x BN, wave
-// tile BM/2 x BN/2 made of 32 x 32 MFMA tiles):
+// Kernel layout (WM x WN waves of 64 lanes -- 4 in the shapes launched,
+// 2 x 2 for 256 x 256, 1 x 4 for 224 x 256, 4 x 1 for 256 x 224; the
+// template also builds 8 -- block tile BM x BN, wave tile BM/WM x BN/WN made
+// of 32 x 32 MFMA tiles):
 //   - V_MFMA_SCALE_F32_32X32X64_F8F6F4 with both operands FP4 (format 4) and
 //     fp32 accumulation.  Operand lane l supplies row (l mod 32) and k-half
 //     (l div 32) of a 32 x 64 slice: 32 consecutive k = one 16-byte code
@@ -53,7 +55,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
@@ -122,7 +123,7 @@ __device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict_
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool KTAIL>
-__global__ __launch_bounds__(kThreads) void gemm_mx_tn(
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, float* __restrict__ C,
     int tiles_m, int tiles_n) {
@@ -138,10 +139,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA tiles per wave
     // scale rows are fetched for BM / BN rounded up to whole instructions
     // over the four waves (the extra rows are never read)
-    constexpr int BMP = (BM + 4 * SRPI - 1) / (4 * SRPI) * (4 * SRPI);
-    constexpr int BNP = (BN + 4 * SRPI - 1) / (4 * SRPI) * (4 * SRPI);
-    constexpr int LA = BM / RPI / 4, LB = BN / RPI / 4;        // code DMAs per wave per stage
-    constexpr int SLA = BMP / SRPI / 4, SLB = BNP / SRPI / 4;  // scale DMAs per wave per stage
+    constexpr int NW = WM * WN, NT = 64 * NW;      // waves, threads
+    constexpr int BMP = (BM + NW * SRPI - 1) / (NW * SRPI) * (NW * SRPI);
+    constexpr int BNP = (BN + NW * SRPI - 1) / (NW * SRPI) * (NW * SRPI);
+    constexpr int LA = BM / RPI / NW, LB = BN / RPI / NW;        // code DMAs per wave per stage
+    constexpr int SLA = BMP / SRPI / NW, SLB = BNP / SRPI / NW;  // scale DMAs per wave per stage
     constexpr int DMA_PER_STAGE = LA + LB + (KTAIL ? 0 : SLA + SLB);
     constexpr int kCodesA = 0, kCodesB = BM * RB;
     constexpr int kScA = (BM + BN) * RB, kScB = kScA + BMP * SBY;
@@ -149,8 +151,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int D = NBUF - 1;                    // stages of DMA in flight
     static_assert(BK == 256, "a stage is one 8-block scale group");
     static_assert(NBUF == 2 || NBUF == 4, "stage ring");
-    static_assert(WM * WN == 4 && TM % 32 == 0 && TN % 32 == 0, "wave layout");
-    static_assert(BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "code DMA split over the waves");
+    static_assert((NW == 4 || NW == 8) && TM % 32 == 0 && TN % 32 == 0, "wave layout");
+    static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "code DMA split over the waves");
     static_assert(NBUF * kStage <= 160 * 1024, "LDS");
     // Stage buffers as distinct arrays: the compiler can then tell that
     // fragment reads of one do not wait on DMA still landing in another.
@@ -248,14 +250,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
                 for (int i = 0; i < SLB; ++i)
                     dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, 0);
             } else {
-                for (int r = tid; r < BM; r += kThreads) {
+                for (int r = tid; r < BM; r += NT) {
                     const int64_t g = m0 + r < M ? m0 + r : M - 1;
     #pragma unroll
                     for (int w = 0; w < SW; ++w)
                         reinterpret_cast<uint32_t*>(base + kScA + r * SBY)[w] =
                             zero ? 0u : scale_word_masked(SA, M, g, ks, kt, w);
                 }
-                for (int r = tid; r < BN; r += kThreads) {
+                for (int r = tid; r < BN; r += NT) {
                     const int64_t g = n0 + r < N ? n0 + r : N - 1;
     #pragma unroll
                     for (int w = 0; w < SW; ++w)
@@ -446,10 +448,10 @@ hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
     const int64_t grid = tm * tn < cu_count() ? tm * tn : cu_count();
     if (K % BK == 0) {
         hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, false>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+                           dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
     } else {
         hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, true>), dim3((unsigned)grid),
-                           dim3(kThreads), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+                           dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
     }
     return hipGetLastError();
 }
