@@ -19,6 +19,7 @@ import torch
 AXIS_COLS, AXIS_ROWS = 0, 1
 HAD_NONE, HAD_DET, HAD_SIGNED = 0, 1, 2
 RTN, SR = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4.so")
@@ -49,6 +50,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
         fn.restype = i32
+    L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i32, vp]
+    L.fp4_gemm_mx.restype = i32
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, u64, i32, u64, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
     L.nvfp4_quantize.restype = i32
@@ -159,6 +162,29 @@ def fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=None, stream=None):
     if xtq.shape[1] * 2 != T or tuple(dyts.shape) != _sshape(N, T) or tuple(xts.shape) != _sshape(K, T):
         raise ValueError("wgrad operand shapes disagree")
     return _gemm(lib().fp4_gemm_wgrad, dytq, dyts, xtq, xts, T, N, K, (N, K), out, stream)
+
+
+def fp4_gemm_mx(aq, as_, bq, bs, out=None, out_dtype: int = OUT_F32, accumulate: bool = False,
+                stream=None):
+    """C[M, N] = A B^T (+ C when accumulate) from aq [M, Kc/2] and bq [N, Kc/2]
+    (both blocked along Kc); C fp32 or bf16 (see include/fp4.h)."""
+    M, Kc, N = aq.shape[0], aq.shape[1] * 2, bq.shape[0]
+    if bq.shape[1] * 2 != Kc or tuple(as_.shape) != _sshape(M, Kc) or tuple(bs.shape) != _sshape(N, Kc):
+        raise ValueError("operand shapes disagree")
+    for t, n in ((aq, "a codes"), (as_, "a scales"), (bq, "b codes"), (bs, "b scales")):
+        _need(t, torch.uint8, n)
+    dt = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16}[out_dtype]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing out")
+        out = torch.empty((M, N), dtype=dt, device=aq.device)
+    _need(out, dt, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must have shape %s" % ((M, N),))
+    _check(lib().fp4_gemm_mx(aq.data_ptr(), as_.data_ptr(), bq.data_ptr(), bs.data_ptr(), M, N, Kc,
+                             out.data_ptr(), out_dtype, int(bool(accumulate)),
+                             _stream_ptr(stream, aq.device)))
+    return out
 
 
 def nvfp4_workspace_bytes(rows: int, cols: int) -> int:

@@ -22,7 +22,7 @@ constexpr int64_t kMaxTiles = INT64_C(1) << 24;
 fp4_status from_hip(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_LAUNCH; }
 
 fp4_status check_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
-                      const float* c, int64_t M, int64_t N, int64_t K) {
+                      const void* c, int64_t M, int64_t N, int64_t K) {
     if (!aq || !as || !bq || !bs || !c) return FP4_ERR_NULL;
     if (M <= 0 || N <= 0 || K <= 0 || K % 32) return FP4_ERR_SHAPE;
     if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N) || M > INT32_MAX ||
@@ -38,10 +38,12 @@ fp4_status check_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, c
 }
 
 fp4_status run_gemm(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
-                    int64_t M, int64_t N, int64_t K, float* c, void* stream) {
+                    int64_t M, int64_t N, int64_t K, void* c, int out_bf16, int accumulate,
+                    void* stream) {
     const fp4_status s = check_gemm(aq, as, bq, bs, c, M, N, K);
     if (s != FP4_OK) return s;
-    return from_hip(fp4dev::launch_gemm_mx(aq, as, bq, bs, M, N, K, c, (hipStream_t)stream));
+    return from_hip(fp4dev::launch_gemm_mx(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate,
+                                           (hipStream_t)stream));
 }
 
 }  // namespace
@@ -69,19 +71,27 @@ fp4_status fp4_hadamard_quantize(const void* x_bf16, int64_t rows, int64_t cols,
 fp4_status fp4_gemm_fprop(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
                           const uint8_t* ws, int64_t T, int64_t N, int64_t K, float* y,
                           void* stream) {
-    return run_gemm(xq, xs, wq, ws, T, N, K, y, stream);        // [T,K] x [N,K]^T
+    return run_gemm(xq, xs, wq, ws, T, N, K, y, 0, 0, stream);        // [T,K] x [N,K]^T
 }
 
 fp4_status fp4_gemm_dgrad(const uint8_t* dyq, const uint8_t* dys, const uint8_t* wtq,
                           const uint8_t* wts, int64_t T, int64_t N, int64_t K, float* dx,
                           void* stream) {
-    return run_gemm(dyq, dys, wtq, wts, T, K, N, dx, stream);   // [T,N] x [K,N]^T
+    return run_gemm(dyq, dys, wtq, wts, T, K, N, dx, 0, 0, stream);   // [T,N] x [K,N]^T
 }
 
 fp4_status fp4_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, const uint8_t* xtq,
                           const uint8_t* xts, int64_t T, int64_t N, int64_t K, float* dw,
                           void* stream) {
-    return run_gemm(dytq, dyts, xtq, xts, N, K, T, dw, stream);  // [N,T] x [K,T]^T
+    return run_gemm(dytq, dyts, xtq, xts, N, K, T, dw, 0, 0, stream);  // [N,T] x [K,T]^T
+}
+
+fp4_status fp4_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                       int64_t M, int64_t N, int64_t Kc, void* c, fp4_out_dtype out,
+                       int accumulate, void* stream) {
+    if (out != FP4_OUT_F32 && out != FP4_OUT_BF16) return FP4_ERR_ENUM;
+    if (accumulate != 0 && accumulate != 1) return FP4_ERR_ENUM;
+    return run_gemm(aq, as, bq, bs, M, N, Kc, c, out == FP4_OUT_BF16 ? 1 : 0, accumulate, stream);
 }
 
 size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols) {
@@ -117,7 +127,7 @@ const char* fp4_status_string(fp4_status status) {
         case FP4_ERR_NULL: return "FP4_ERR_NULL: a required pointer is NULL";
         case FP4_ERR_SHAPE: return "FP4_ERR_SHAPE: bad size or contraction not a multiple of the block";
         case FP4_ERR_ALIGN: return "FP4_ERR_ALIGN: pointer not 16-byte aligned";
-        case FP4_ERR_ENUM: return "FP4_ERR_ENUM: unknown axis, Hadamard mode/size or rounding";
+        case FP4_ERR_ENUM: return "FP4_ERR_ENUM: unknown axis, Hadamard mode/size, rounding, output type or flag";
         case FP4_ERR_LAUNCH: return "FP4_ERR_LAUNCH: HIP kernel launch failed";
         case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE: workspace missing or too small";
     }

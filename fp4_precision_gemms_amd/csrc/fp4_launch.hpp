@@ -12,10 +12,11 @@ hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, 
                            uint64_t sign_seed, int rnd, uint64_t sr_seed, uint8_t* codes,
                            uint8_t* scales, hipStream_t st);
 
-// C[M, N] (fp32, row-major) = A[M, K] B[N, K]^T over MXFP4 operands.
+// C[M, N] (row-major; fp32, or bf16 when out_bf16) = A[M, K] B[N, K]^T
+// (+ C when accumulate) over MXFP4 operands.
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
-                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
-                          hipStream_t st);
+                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* c,
+                          int out_bf16, int accumulate, hipStream_t st);
 
 // NVFP4 quantization; amax_dev is either the caller's amax_in or the
 // workspace the amax pass writes.

@@ -122,10 +122,20 @@ __device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict_
     return word;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool KTAIL>
+// Round-to-nearest-even binary32 -> bfloat16 (NaN -> the quiet NaN 0x7FC0).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+
+// OBF16: C is bfloat16 (else fp32); ACC: C = A B^T + C (else C = A B^T), the
+// sum formed in fp32 before the output rounding.
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool KTAIL, bool OBF16, bool ACC>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, float* __restrict__ C,
+    const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
     int tiles_m, int tiles_n) {
     constexpr int RB = BK / 2;                     // code bytes per row per stage
     constexpr int CPR = RB / 16;                   // 16-byte chunks per row
@@ -399,26 +409,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
 
         // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
         // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.
+        // Each (i, j, q) is four consecutive n of one row: one 16-byte fp32
+        // or 8-byte bf16 access when N % 4 == 0 and all four exist.
         const bool vec_store = (N % 4) == 0;
     #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int64_t m = m0 + wm * TM + i * 32 + l32;
             if (m >= M) continue;
-            float* crow = C + m * N;
     #pragma unroll
             for (int j = 0; j < FN; ++j) {
     #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t n = n0 + wn * TN + j * 32 + 8 * q + 4 * h;
-                    const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                 acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                    if (vec_store && n + 4 <= N) {
-                        *reinterpret_cast<float4*>(crow + n) = v;
+                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                  acc[i][j][4 * q + 3]};
+                    if constexpr (OBF16) {
+                        uint16_t* crow = reinterpret_cast<uint16_t*>(C) + m * N;
+                        if (vec_store && n + 4 <= N) {
+                            uint2* p = reinterpret_cast<uint2*>(crow + n);
+                            if constexpr (ACC) {
+                                const uint2 o = *p;
+                                v[0] += bf16_value(o.x & 0xFFFFu); v[1] += bf16_value(o.x >> 16);
+                                v[2] += bf16_value(o.y & 0xFFFFu); v[3] += bf16_value(o.y >> 16);
+                            }
+                            *p = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                            bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+                        } else {
+                            for (int e = 0; e < 4; ++e) {
+                                if (n + e >= N) break;
+                                const float old = ACC ? bf16_value(crow[n + e]) : 0.0f;
+                                crow[n + e] = (uint16_t)bf16_rne(ACC ? v[e] + old : v[e]);
+                            }
+                        }
                     } else {
-                        if (n < N) crow[n] = v.x;
-                        if (n + 1 < N) crow[n + 1] = v.y;
-                        if (n + 2 < N) crow[n + 2] = v.z;
-                        if (n + 3 < N) crow[n + 3] = v.w;
+                        float* crow = reinterpret_cast<float*>(C) + m * N;
+                        if (vec_store && n + 4 <= N) {
+                            float4* p = reinterpret_cast<float4*>(crow + n);
+                            if constexpr (ACC) {
+                                const float4 o = *p;
+                                v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+                            }
+                            *p = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+                            for (int e = 0; e < 4; ++e) {
+                                if (n + e >= N) break;
+                                crow[n + e] = ACC ? v[e] + crow[n + e] : v[e];
+                            }
+                        }
                     }
                 }
             }
@@ -440,18 +477,32 @@ int cu_count() {
     return counts[dev];
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM>
-hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
-                        const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
-                        hipStream_t st) {
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool OBF16, bool ACC>
+void launch_kernel(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                   int64_t M, int64_t N, int64_t K, void* c, hipStream_t st) {
     const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const int64_t grid = tm * tn < cu_count() ? tm * tn : cu_count();
     if (K % BK == 0) {
-        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, false>), dim3((unsigned)grid),
-                           dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, false, OBF16, ACC>),
+                           dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K,
+                           c, (int)tm, (int)tn);
     } else {
-        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, true>), dim3((unsigned)grid),
-                           dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K, c, (int)tm, (int)tn);
+        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, true, OBF16, ACC>),
+                           dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K,
+                           c, (int)tm, (int)tn);
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM>
+hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
+                        const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* c, int out_bf16,
+                        int accumulate, hipStream_t st) {
+    if (out_bf16) {
+        if (accumulate) launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, true, true>(aq, as, bq, bs, M, N, K, c, st);
+        else launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, true, false>(aq, as, bq, bs, M, N, K, c, st);
+    } else {
+        if (accumulate) launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, false, true>(aq, as, bq, bs, M, N, K, c, st);
+        else launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, false, false>(aq, as, bq, bs, M, N, K, c, st);
     }
     return hipGetLastError();
 }
@@ -459,8 +510,8 @@ hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
 }  // namespace
 
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
-                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, float* c,
-                          hipStream_t st) {
+                          const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* c,
+                          int out_bf16, int accumulate, hipStream_t st) {
     // Tile shape: the persistent grid runs ceil(tiles / CUs) rounds of one
     // tile per CU, each costing about the tile's area, so pick the shape with
     // the least rounds x area (256 x 256 unless a 224-row or -column tile
@@ -472,10 +523,10 @@ hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* b
     };
     const int64_t c256 = cost(256, 256), cm = cost(224, 256), cn = cost(256, 224);
     if (cm < c256 && cm <= cn)
-        return launch_tiles<224, 256, 1, 4, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, st);
+        return launch_tiles<224, 256, 1, 4, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
     if (cn < c256)
-        return launch_tiles<256, 224, 4, 1, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, st);
-    return launch_tiles<256, 256, 2, 2, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, st);
+        return launch_tiles<256, 224, 4, 1, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
+    return launch_tiles<256, 256, 2, 2, 256, 2, 8>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
 }
 
 }  // namespace fp4dev

@@ -55,7 +55,8 @@ typedef enum {
     FP4_ERR_SHAPE = 2,   /* size <= 0, contraction not a multiple of the block, */
                          /* or a size whose byte count overflows int64          */
     FP4_ERR_ALIGN = 3,   /* a pointer is not 16-byte aligned                    */
-    FP4_ERR_ENUM = 4,    /* unknown axis / Hadamard mode / size / rounding      */
+    FP4_ERR_ENUM = 4,    /* unknown axis / Hadamard mode / size / rounding /    */
+                         /* output type / flag                                  */
     FP4_ERR_LAUNCH = 5,  /* the HIP runtime refused a kernel launch             */
     FP4_ERR_WORKSPACE = 6 /* workspace missing or smaller than required         */
 } fp4_status;
@@ -157,6 +158,35 @@ fp4_status fp4_gemm_dgrad(const uint8_t* dyq, const uint8_t* dys, const uint8_t*
 fp4_status fp4_gemm_wgrad(const uint8_t* dytq, const uint8_t* dyts, const uint8_t* xtq,
                           const uint8_t* xts, int64_t T, int64_t N, int64_t K,
                           float* dw, void* stream);
+
+/* Output element type of fp4_gemm_mx. */
+typedef enum {
+    FP4_OUT_F32 = 0,     /* binary32                                              */
+    FP4_OUT_BF16 = 1     /* bfloat16, rounded to nearest even from the fp32 result */
+} fp4_out_dtype;
+
+/*
+ * fp4_gemm_mx -- the same scaled-FP4 product as the three role entry points,
+ * C[m, n] = sum_k a[m, k] b[n, k] over MXFP4 operands aq/as [M, Kc] and
+ * bq/bs [N, Kc] (codes and k-grouped scales along the contraction, as
+ * fp4_hadamard_quantize writes them), with two output options:
+ *   out = FP4_OUT_F32 or FP4_OUT_BF16: the element type of C (row-major
+ *         [M, N]); bf16 is the fp32 result rounded to nearest even (NaN ->
+ *         0x7FC0).
+ *   accumulate = 0: C is overwritten; 1: C = A B^T + C, the old value read
+ *         from C (widened to fp32) and added to the fp32 product before the
+ *         output rounding.
+ * Fprop, Dgrad and Wgrad are fp4_gemm_mx(A, B) with the operands named in
+ * their comments above, fp32 output and accumulate = 0.  [AMD-MXFP4,
+ * "Поисковая экспериментальная работа: корень нестабильности"]: the three
+ * GEMMs in MXFP4; gradient accumulation and a bf16 activation output are
+ * what a training step adds around them.
+ * Requirements as for the role entry points; out and accumulate outside
+ * their values give FP4_ERR_ENUM.
+ */
+fp4_status fp4_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                       int64_t M, int64_t N, int64_t Kc, void* c, fp4_out_dtype out,
+                       int accumulate, void* stream);
 
 /*
  * nvfp4_quantize -- NVFP4 quantization of bf16 x[rows, cols] along cols in

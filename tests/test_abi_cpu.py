@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp4_hadamard_quantize", "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad",
-              "nvfp4_quantize", "nvfp4_workspace_bytes", "fp4_status_string"):
+              "fp4_gemm_mx", "nvfp4_quantize", "nvfp4_workspace_bytes", "fp4_status_string"):
         assert n in names
 
 
@@ -105,6 +105,21 @@ def test_gemm_errors(L, name):
     dims[(contraction + 1) % 3] = 48
     assert call(dims=tuple(dims), out=MIS) == ERR_ALIGN
     assert call(ptrs=(A, MIS, A, A)) == ERR_ALIGN
+
+
+def test_gemm_mx_errors(L):
+    def call(ptrs=(A, A, A, A), dims=(64, 64, 64), out=A, dtype=0, acc=0):
+        return L.fp4_gemm_mx(*ptrs, *dims, out, dtype, acc, None)
+
+    assert call(dtype=2) == ERR_ENUM
+    assert call(dtype=-1) == ERR_ENUM
+    assert call(acc=2) == ERR_ENUM
+    assert call(ptrs=(A, None, A, A)) == ERR_NULL
+    assert call(out=None, dtype=1) == ERR_NULL
+    assert call(dims=(64, 64, 48)) == ERR_SHAPE
+    assert call(dims=(64, 0, 64), dtype=1, acc=1) == ERR_SHAPE
+    assert call(out=MIS, dtype=1) == ERR_ALIGN
+    assert call(out=MIS, acc=1) == ERR_ALIGN
 
 
 def test_nvfp4_errors(L):
