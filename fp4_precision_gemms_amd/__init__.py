@@ -50,6 +50,9 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
         fn.restype = i32
+    L.fp4_hadamard_quantize_dual.argtypes = [vp, i64, i64, i32, i32, u64, i32, u64, vp, vp,
+                                             i32, i32, u64, i32, u64, vp, vp, vp]
+    L.fp4_hadamard_quantize_dual.restype = i32
     L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i32, vp]
     L.fp4_gemm_mx.restype = i32
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, u64, i32, u64, vp, vp, vp, vp, vp,
@@ -120,6 +123,26 @@ def fp4_hadamard_quantize(x: torch.Tensor, axis: int = AXIS_COLS, had_n: int = 3
                                        codes.data_ptr(), scales.data_ptr(),
                                        _stream_ptr(stream, x.device)))
     return codes, scales
+
+
+def fp4_hadamard_quantize_dual(x: torch.Tensor, had_n_rows: int = 32, had_rows: int = HAD_NONE,
+                               sign_seed_rows: int = 0, rnd_rows: int = RTN, sr_seed_rows: int = 0,
+                               had_n_cols: int = 32, had_cols: int = HAD_NONE, sign_seed_cols: int = 0,
+                               rnd_cols: int = RTN, sr_seed_cols: int = 0, stream=None):
+    """Both quantizations of bf16 x[rows, cols] from one read: (codes, scales)
+    along rows (as AXIS_ROWS) and along cols (as AXIS_COLS), each with its own
+    rotation and rounding (see include/fp4.h)."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    (cr, sr), (cc, sc) = mx_shapes(rows, cols, AXIS_ROWS), mx_shapes(rows, cols, AXIS_COLS)
+    dev = x.device
+    out = [torch.empty(sh, dtype=torch.uint8, device=dev) for sh in (cr, sr, cc, sc)]
+    m = 2 ** 64 - 1
+    _check(lib().fp4_hadamard_quantize_dual(
+        x.data_ptr(), rows, cols, had_n_rows, had_rows, sign_seed_rows & m, rnd_rows, sr_seed_rows & m,
+        out[0].data_ptr(), out[1].data_ptr(), had_n_cols, had_cols, sign_seed_cols & m, rnd_cols,
+        sr_seed_cols & m, out[2].data_ptr(), out[3].data_ptr(), _stream_ptr(stream, dev)))
+    return tuple(out)
 
 
 def _gemm(fn, aq, as_, bq, bs, T, N, K, out_shape, out, stream):

@@ -68,6 +68,31 @@ fp4_status fp4_hadamard_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                                             (hipStream_t)stream));
 }
 
+fp4_status fp4_hadamard_quantize_dual(const void* x_bf16, int64_t rows, int64_t cols,
+                                      int had_n_rows, fp4_hadamard had_rows, uint64_t sign_seed_rows,
+                                      fp4_rounding rnd_rows, uint64_t sr_seed_rows,
+                                      uint8_t* codes_rows, uint8_t* scales_rows, int had_n_cols,
+                                      fp4_hadamard had_cols, uint64_t sign_seed_cols,
+                                      fp4_rounding rnd_cols, uint64_t sr_seed_cols,
+                                      uint8_t* codes_cols, uint8_t* scales_cols, void* stream) {
+    for (const fp4_hadamard h : {had_rows, had_cols})
+        if (h != FP4_HAD_NONE && h != FP4_HAD_DET && h != FP4_HAD_SIGNED) return FP4_ERR_ENUM;
+    if (had_rows != FP4_HAD_NONE && had_n_rows != 16 && had_n_rows != 32) return FP4_ERR_ENUM;
+    if (had_cols != FP4_HAD_NONE && had_n_cols != 16 && had_n_cols != 32) return FP4_ERR_ENUM;
+    for (const fp4_rounding r : {rnd_rows, rnd_cols})
+        if (r != FP4_RTN && r != FP4_SR) return FP4_ERR_ENUM;
+    if (!x_bf16 || !codes_rows || !scales_rows || !codes_cols || !scales_cols) return FP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || !product_ok(rows, cols) || rows % 32 || cols % 32)
+        return FP4_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(codes_rows) || !aligned16(scales_rows) ||
+        !aligned16(codes_cols) || !aligned16(scales_cols))
+        return FP4_ERR_ALIGN;
+    return from_hip(fp4dev::launch_quant_mx_dual(
+        x_bf16, rows, cols, had_n_rows, (int)had_rows, sign_seed_rows, (int)rnd_rows, sr_seed_rows,
+        codes_rows, scales_rows, had_n_cols, (int)had_cols, sign_seed_cols, (int)rnd_cols,
+        sr_seed_cols, codes_cols, scales_cols, (hipStream_t)stream));
+}
+
 fp4_status fp4_gemm_fprop(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
                           const uint8_t* ws, int64_t T, int64_t N, int64_t K, float* y,
                           void* stream) {

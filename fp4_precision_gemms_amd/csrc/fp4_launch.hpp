@@ -12,6 +12,15 @@ hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, 
                            uint64_t sign_seed, int rnd, uint64_t sr_seed, uint8_t* codes,
                            uint8_t* scales, hipStream_t st);
 
+// Both MXFP4 quantizations of x from one read: along rows (codes_r/scales_r,
+// as axis 1) and along cols (codes_c/scales_c, as axis 0), each with its own
+// rotation and rounding.  Needs rows % 32 == 0 and cols % 32 == 0.
+hipError_t launch_quant_mx_dual(const void* x, int64_t rows, int64_t cols, int had_n_r, int had_r,
+                                uint64_t sign_seed_r, int rnd_r, uint64_t sr_seed_r, uint8_t* codes_r,
+                                uint8_t* scales_r, int had_n_c, int had_c, uint64_t sign_seed_c,
+                                int rnd_c, uint64_t sr_seed_c, uint8_t* codes_c, uint8_t* scales_c,
+                                hipStream_t st);
+
 // C[M, N] (row-major; fp32, or bf16 when out_bf16) = A[M, K] B[N, K]^T
 // (+ C when accumulate) over MXFP4 operands.
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,

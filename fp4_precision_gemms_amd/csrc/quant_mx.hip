@@ -302,6 +302,48 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* 
 
 constexpr int kTileCols = 256;           // columns per block, one per thread
 
+// Rotation, scale and codes of one 32-element block held by one thread: a[]
+// holds the block's values in order; gbase is the logical index (in the
+// quantized [R, C] layout) of the block's first element divided by 4, the SR
+// counter of its first four elements.  Returns the scale byte; wd gets the
+// 16 code bytes (zero for a NaN / infinite block).
+template <int HADN, bool SR>
+__device__ __forceinline__ uint32_t quant_block32(float* a, uint32_t sign_word, float norm,
+                                                  uint64_t sr_seed, uint64_t gbase, uint32_t* wd) {
+    if constexpr (HADN != 0) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) a[r] = flip_if(a[r], (sign_word >> (r % HADN)) & 1u);
+#pragma unroll
+        for (int o = 0; o < 32; o += HADN) butterflies<HADN>(a + o);
+    }
+    uint32_t m = max_abs_bits<32>(a);
+    if constexpr (HADN != 0) {
+        m = __float_as_uint(__uint_as_float(m) * norm) & 0x7FFFFFFFu;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) a[r] = a[r] * norm;
+    }
+    const uint32_t byte = e8m0_from_amax_bits(m);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wd[k] = 0;
+    if (byte != 255u) {
+        if (!SR && byte != 0u) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wd[k] = encode8_hw(a + 8 * k, byte);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+                if constexpr (SR) {
+                    u0 = stream4(sr_seed, 0u, gbase + 2 * k);
+                    u1 = stream4(sr_seed, 0u, gbase + 2 * k + 1);
+                }
+                wd[k] = encode8_sw<SR>(a + 8 * k, byte, u0, u1);
+            }
+        }
+    }
+    return byte;
+}
+
 // s_waitcnt vmcnt(N) (N <= 63), leaving the other counters alone.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -333,10 +375,17 @@ __device__ __forceinline__ void wait_tile(int t) {
 // encodes them; at the end the TB blocks' codes of a column (16 TB
 // contiguous bytes) leave through LDS in column-major store instructions and
 // the TB scale bytes as one word.  Needs cols % 8 == 0.
-template <int HADN, bool SR, int TB>
+//
+// HADN_C >= 0 adds a second output from the same tiles: x quantized along
+// cols (blocks of 32 consecutive columns, rotation size HADN_C, 0 = none,
+// rounding to nearest), one (row, 32-column block) of each tile per thread,
+// read as four 16-byte LDS loads.  Needs cols % 32 == 0 then.
+template <int HADN, bool SR, int TB, int HADN_C>
 __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
-    uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    uint32_t sign_word_c, float norm_c, uint64_t sr_seed_c, uint8_t* __restrict__ codes_c,
+    uint8_t* __restrict__ scales_c) {
     static_assert(TB == 2 || TB == 4 || TB == 8, "blocks per workgroup");
     constexpr int kTileBlocks = TB;
     __shared__ __attribute__((aligned(1024))) uint16_t tile[kTileBlocks][32 * kTileCols];
@@ -351,7 +400,10 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)x, (short)0, (int)(rows * cols * 2), 0x00020000);
     // DMA instruction j of a tile (4 per wave) covers rows 2j, 2j+1:
-    // lane i -> row 2j + i / 32, bytes 16 (i mod 32) of the row segment.
+    // lane i -> row 2j + i / 32, LDS slot i mod 32 of the row segment, which
+    // holds 16-byte chunk (i mod 32) XOR (row mod 4): the swizzle keeps the
+    // per-column reads conflict-free and makes the per-row 16-byte reads of
+    // the along-cols output conflict-free too.
     // Every tile is issued, also those past the last row (they read zeros),
     // so that the wait counts below are the same for every workgroup.
     const int64_t nbytes = rows * cols * 2;
@@ -361,11 +413,16 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
         for (int k = 0; k < 4; ++k) {
             const int j = wave * 4 + k;
             const int64_t row = (rb0 + t) * 32 + 2 * j + (lane >> 5);
-            const int64_t o = (row * cols + c0) * 2 + (lane & 31) * 16;
+            const int64_t o = (row * cols + c0) * 2 + (int64_t)((((lane & 31) ^ (int)(row & 3))) * 16);
             dma16_to_lds(rx, (uint8_t*)tile[t] + j * 1024, o < nbytes ? (uint32_t)o : 0x80000000u);
         }
     }
     const int64_t col = c0 + tid;
+    // LDS position (bf16 units, within a row) of this thread's column for row
+    // mod 4 = q: its 8-column chunk XOR q
+    int colpos[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) colpos[q] = (((tid >> 3) ^ q) << 3) | (tid & 7);
     uint32_t wd[kTileBlocks][4] = {};
     uint64_t sword = 0;
 #pragma unroll
@@ -379,37 +436,34 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         float a[32];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) a[r] = __uint_as_float((uint32_t)tile[t][r * kTileCols + tid] << 16);
-        if constexpr (HADN != 0) {
-#pragma unroll
-            for (int r = 0; r < 32; ++r) a[r] = flip_if(a[r], (sign_word >> (r % HADN)) & 1u);
-#pragma unroll
-            for (int o = 0; o < 32; o += HADN) butterflies<HADN>(a + o);
-        }
-        uint32_t m = max_abs_bits<32>(a);
-        if constexpr (HADN != 0) {
-            m = __float_as_uint(__uint_as_float(m) * norm) & 0x7FFFFFFFu;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) a[r] = a[r] * norm;
-        }
-        const uint32_t byte = e8m0_from_amax_bits(m);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) wd[t][k] = 0;
-        if (byte != 255u) {
-            if (!SR && byte != 0u) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) wd[t][k] = encode8_hw(a + 8 * k, byte);
-            } else {
-                const uint64_t gbase = ((uint64_t)col * (uint64_t)rows + (uint64_t)(rb0 + t) * 32) >> 2;
+        for (int r = 0; r < 32; ++r) a[r] = __uint_as_float((uint32_t)tile[t][r * kTileCols + colpos[r & 3]] << 16);
+        const uint64_t gbase = ((uint64_t)col * (uint64_t)rows + (uint64_t)(rb0 + t) * 32) >> 2;
+        const uint32_t byte = quant_block32<HADN, SR>(a, sign_word, norm, sr_seed, gbase, wd[t]);
+        if constexpr (HADN_C >= 0) {
+            // the same tile along cols: each 16-lane group of a wave takes 4
+            // rows x 4 blocks, so with the chunk swizzle its 16-byte reads of
+            // chunk k hit 16 different bank groups
+            const int grp = lane >> 4;
+            const int r = 8 * wave + 4 * (grp & 1) + ((lane >> 2) & 3), b = 4 * (grp >> 1) + (lane & 3);
+            const int64_t row = (rb0 + t) * 32 + r, cb = c0 + 32 * b;
+            if (cb < cols) {
+                float ar[32];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
-                    if constexpr (SR) {
-                        u0 = stream4(sr_seed, 0u, gbase + 2 * k);
-                        u1 = stream4(sr_seed, 0u, gbase + 2 * k + 1);
-                    }
-                    wd[t][k] = encode8_sw<SR>(a + 8 * k, byte, u0, u1);
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        &tile[t][r * kTileCols + (((4 * b + k) ^ (r & 3)) << 3)]);
+                    ar[8 * k + 0] = bf16_lo(v.x); ar[8 * k + 1] = bf16_hi(v.x);
+                    ar[8 * k + 2] = bf16_lo(v.y); ar[8 * k + 3] = bf16_hi(v.y);
+                    ar[8 * k + 4] = bf16_lo(v.z); ar[8 * k + 5] = bf16_hi(v.z);
+                    ar[8 * k + 6] = bf16_lo(v.w); ar[8 * k + 7] = bf16_hi(v.w);
                 }
+                uint32_t wc[4];
+                const uint64_t gb = ((uint64_t)row * (uint64_t)cols + (uint64_t)cb) >> 2;
+                const uint32_t bc = quant_block32<HADN_C, false>(ar, sign_word_c, norm_c, sr_seed_c, gb, wc);
+                *reinterpret_cast<uint4*>(codes_c + row * (cols / 2) + cb / 2) =
+                    make_uint4(wc[0], wc[1], wc[2], wc[3]);
+                const int64_t blk = cb / 32;
+                scales_c[((blk >> 3) * rows + row) * 8 + (blk & 7)] = (uint8_t)bc;
             }
         }
         sword |= (uint64_t)byte << (8 * t);
@@ -490,9 +544,10 @@ hipError_t dispatch_rows_cpl(const void* x, int64_t rows, int64_t cols, uint32_t
         const int64_t gx = (cols + kTileCols - 1) / kTileCols;
         constexpr int TB = kRowsLdsBlocks;
         const int64_t gy = (rows / 32 + TB - 1) / TB;
-        hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB>), dim3((unsigned)gx, (unsigned)gy),
+        hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, -1>), dim3((unsigned)gx, (unsigned)gy),
                            dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
-                           sr_seed, codes, scales);
+                           sr_seed, codes, scales, 0u, 1.0f, (uint64_t)0, (uint8_t*)nullptr,
+                           (uint8_t*)nullptr);
         return hipGetLastError();
     }
     if (cols % 4 == 0) return launch_rows<4, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
@@ -512,6 +567,43 @@ hipError_t dispatch_rnd(int axis, bool sr, const void* x, int64_t rows, int64_t 
               : dispatch_rows_cpl<HADN, false>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
 }
 
+// Both outputs from one pass over the tiles (the rows output is the one the
+// kernel's template arguments HADN / SR describe).
+template <int HADN, bool SR, int HADN_C>
+hipError_t launch_dual(const void* x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
+                       uint64_t sr_seed, uint8_t* codes, uint8_t* scales, uint32_t sign_word_c,
+                       float norm_c, uint64_t sr_seed_c, uint8_t* codes_c,
+                       uint8_t* scales_c, hipStream_t st) {
+    constexpr int TB = kRowsLdsBlocks;
+    const int64_t gx = (cols + kTileCols - 1) / kTileCols;
+    const int64_t gy = (rows / 32 + TB - 1) / TB;
+    hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, HADN_C>), dim3((unsigned)gx, (unsigned)gy),
+                       dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
+                       sr_seed, codes, scales, sign_word_c, norm_c, sr_seed_c, codes_c, scales_c);
+    return hipGetLastError();
+}
+
+template <int HADN, bool SR>
+hipError_t dispatch_dual_c(int hadn_c, const void* x, int64_t rows, int64_t cols, uint32_t sign_word,
+                           float norm, uint64_t sr_seed, uint8_t* codes, uint8_t* scales,
+                           uint32_t sign_word_c, float norm_c, uint64_t sr_seed_c,
+                           uint8_t* codes_c, uint8_t* scales_c, hipStream_t st) {
+    if (hadn_c == 0)
+        return launch_dual<HADN, SR, 0>(x, rows, cols, sign_word, norm, sr_seed, codes, scales,
+                                        sign_word_c, norm_c, sr_seed_c, codes_c, scales_c, st);
+    if (hadn_c == 16)
+        return launch_dual<HADN, SR, 16>(x, rows, cols, sign_word, norm, sr_seed, codes, scales,
+                                         sign_word_c, norm_c, sr_seed_c, codes_c, scales_c, st);
+    return launch_dual<HADN, SR, 32>(x, rows, cols, sign_word, norm, sr_seed, codes, scales,
+                                     sign_word_c, norm_c, sr_seed_c, codes_c, scales_c, st);
+}
+
+// Rotation size and the binary32 factor fl(1/sqrt(n)) of a (had, had_n) pair.
+int rot_size(int had, int had_n) { return had == 0 ? 0 : had_n; }
+float rot_norm(int n) {
+    return n == 0 ? 1.0f : n == 16 ? 0.25f : __builtin_bit_cast(float, 0x3E3504F3u);
+}
+
 }  // namespace
 
 // Host-side sign word of the randomized transform: bit j of word 0 of the
@@ -529,6 +621,38 @@ uint32_t host_sign_word(int had, uint64_t seed) {
         c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
     }
     return c[0];
+}
+
+hipError_t launch_quant_mx_dual(const void* x, int64_t rows, int64_t cols, int had_n_r, int had_r,
+                                uint64_t sign_seed_r, int rnd_r, uint64_t sr_seed_r, uint8_t* codes_r,
+                                uint8_t* scales_r, int had_n_c, int had_c, uint64_t sign_seed_c,
+                                int rnd_c, uint64_t sr_seed_c, uint8_t* codes_c, uint8_t* scales_c,
+                                hipStream_t st) {
+    if (rows * cols * 2 >= (INT64_C(1) << 31) || rnd_c == 1) {
+        // beyond the fused kernel's 32-bit buffer offsets, or stochastic
+        // rounding on the along-cols output (the fused kernel rounds that
+        // output to nearest only): two passes
+        const hipError_t e = launch_quant_mx(x, rows, cols, 1, had_n_r, had_r, sign_seed_r, rnd_r,
+                                             sr_seed_r, codes_r, scales_r, st);
+        if (e != hipSuccess) return e;
+        return launch_quant_mx(x, rows, cols, 0, had_n_c, had_c, sign_seed_c, rnd_c, sr_seed_c,
+                               codes_c, scales_c, st);
+    }
+    const int nr = rot_size(had_r, had_n_r), nc = rot_size(had_c, had_n_c);
+    const uint32_t sw_r = host_sign_word(had_r, sign_seed_r), sw_c = host_sign_word(had_c, sign_seed_c);
+    const float fr = rot_norm(nr), fc = rot_norm(nc);
+#define FP4_DUAL(HR, SRR)                                                                        \
+    return dispatch_dual_c<HR, SRR>(nc, x, rows, cols, sw_r, fr, sr_seed_r, codes_r, scales_r, \
+                                    sw_c, fc, sr_seed_c, codes_c, scales_c, st)
+    if (rnd_r == 1) {
+        if (nr == 0) FP4_DUAL(0, true);
+        if (nr == 16) FP4_DUAL(16, true);
+        FP4_DUAL(32, true);
+    }
+    if (nr == 0) FP4_DUAL(0, false);
+    if (nr == 16) FP4_DUAL(16, false);
+    FP4_DUAL(32, false);
+#undef FP4_DUAL
 }
 
 hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, int had_n, int had,

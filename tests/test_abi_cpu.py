@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp4_hadamard_quantize", "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad",
-              "fp4_gemm_mx", "nvfp4_quantize", "nvfp4_workspace_bytes", "fp4_status_string"):
+              "fp4_gemm_mx", "fp4_hadamard_quantize_dual", "nvfp4_quantize",
+              "nvfp4_workspace_bytes", "fp4_status_string"):
         assert n in names
 
 
@@ -105,6 +106,25 @@ def test_gemm_errors(L, name):
     dims[(contraction + 1) % 3] = 48
     assert call(dims=tuple(dims), out=MIS) == ERR_ALIGN
     assert call(ptrs=(A, MIS, A, A)) == ERR_ALIGN
+
+
+def test_quantize_dual_errors(L):
+    def call(x=A, rows=64, cols=64, hn=(32, 32), had=(1, 0), rnd=(0, 0), ptrs=(A, A, A, A)):
+        return L.fp4_hadamard_quantize_dual(x, rows, cols, hn[0], had[0], 0, rnd[0], 0, ptrs[0], ptrs[1],
+                                            hn[1], had[1], 0, rnd[1], 0, ptrs[2], ptrs[3], None)
+
+    assert call(had=(3, 0)) == ERR_ENUM
+    assert call(had=(0, 5)) == ERR_ENUM
+    assert call(hn=(8, 32)) == ERR_ENUM
+    assert call(hn=(32, 8), had=(1, 2)) == ERR_ENUM
+    assert call(rnd=(0, 2)) == ERR_ENUM
+    assert call(x=None) == ERR_NULL
+    assert call(ptrs=(A, A, A, None)) == ERR_NULL
+    assert call(rows=48) == ERR_SHAPE                  # both axes are contractions
+    assert call(cols=80) == ERR_SHAPE
+    assert call(rows=0) == ERR_SHAPE
+    assert call(ptrs=(A, A, MIS, A)) == ERR_ALIGN
+    assert call(x=MIS) == ERR_ALIGN
 
 
 def test_gemm_mx_errors(L):
