@@ -235,3 +235,6 @@ def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, r
                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                 _stream_ptr(stream, dev)))
     return codes, scales, tensor_scale
+
+
+from . import linear  # noqa: E402  (the autograd layer built on the calls above)
