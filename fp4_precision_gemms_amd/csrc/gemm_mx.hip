@@ -130,6 +130,17 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
 
+// A 16-byte store of C marked non-temporal: with whole 128-byte lines per
+// instruction the output streams to HBM during the GEMM instead of sitting
+// dirty in the caches until the next kernel's traffic evicts it (measured:
+// the quantizer that follows ran 14 us longer on dY[8192x14336]).  Partial
+// lines must not take this path: non-temporal 16-byte pieces of a line are
+// written to memory one by one.
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_c_line_part(float* p, float4 v) {
+    __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
+}
+
 // OBF16: C is bfloat16 (else fp32); ACC: C = A B^T + C (else C = A B^T), the
 // sum formed in fp32 before the output rounding.
 template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool KTAIL, bool OBF16, bool ACC>
@@ -409,9 +420,54 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
 
         // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
         // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.
+        const bool vec_store = (N % 4) == 0;
+        // fp32 overwrite with N % 4 == 0: the wave's rows go out through LDS
+        // in whole 128-byte lines (TN / 4 lanes per row), so every store
+        // instruction writes full lines.  The stage buffers are free once
+        // every wave is past its last fragment read; each wave stages up to
+        // 32 KB of its tile at a time in its own quarter of them, rows
+        // padded by 16 bytes (conflict-free writes of the accumulator
+        // layout, conflict-free row reads).
+        constexpr int kRowBytes = TN * 4 + 16;
+        constexpr int kLanesPerRow = TN / 4, kRowsPerInst = 64 / kLanesPerRow;
+        constexpr bool kStaged = !OBF16 && !ACC && (64 % kLanesPerRow == 0) && (32 * kRowBytes <= 32768) &&
+                                 (NW == 4) && (kStage >= 65536);
+        if constexpr (kStaged) {
+            if (vec_store) {
+                constexpr int ICH = (32768 / kRowBytes) / 32 < FM ? (32768 / kRowBytes) / 32 : FM;
+                uint8_t* const reg = ((wave >> 1) ? lds1 : lds0) + (wave & 1) * 32768;
+                __syncthreads();                        // all fragment reads of the tile are done
+    #pragma unroll
+                for (int i0 = 0; i0 < FM; i0 += ICH) {
+    #pragma unroll
+                    for (int ii = 0; ii < ICH; ++ii) {
+                        if (i0 + ii >= FM) break;
+    #pragma unroll
+                        for (int j = 0; j < FN; ++j)
+    #pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const int row = ii * 32 + l32, cn = j * 32 + 8 * q + 4 * h;
+                                *reinterpret_cast<float4*>(reg + row * kRowBytes + cn * 4) =
+                                    make_float4(acc[i0 + ii][j][4 * q], acc[i0 + ii][j][4 * q + 1],
+                                                acc[i0 + ii][j][4 * q + 2], acc[i0 + ii][j][4 * q + 3]);
+                            }
+                    }
+                    const int nrows = (FM - i0 < ICH ? FM - i0 : ICH) * 32;
+    #pragma unroll
+                    for (int rr = 0; rr < ICH * 32; rr += kRowsPerInst) {
+                        const int row = rr + lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
+                        if (rr >= nrows) break;
+                        const float4 v = *reinterpret_cast<const float4*>(reg + row * kRowBytes + c4 * 4);
+                        const int64_t m = m0 + wm * TM + i0 * 32 + row, n = n0 + wn * TN + c4;
+                        if (m < M && n + 4 <= N)
+                            store_c_line_part(reinterpret_cast<float*>(C) + m * N + n, v);
+                    }
+                }
+                continue;                               // next tile
+            }
+        }
         // Each (i, j, q) is four consecutive n of one row: one 16-byte fp32
         // or 8-byte bf16 access when N % 4 == 0 and all four exist.
-        const bool vec_store = (N % 4) == 0;
     #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int64_t m = m0 + wm * TM + i * 32 + l32;
