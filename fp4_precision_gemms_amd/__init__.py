@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
     L.fp4_hadamard_quantize_dual.argtypes = [vp, i64, i64, i32, i32, u64, i32, u64, vp, vp,
                                              i32, i32, u64, i32, u64, vp, vp, vp]
     L.fp4_hadamard_quantize_dual.restype = i32
+    L.fp4_wgrad_quantize.argtypes = [vp, vp, i64, i64, i64, i32, i32, u64, i32, u64, u64,
+                                     vp, vp, vp, vp, vp]
+    L.fp4_wgrad_quantize.restype = i32
     L.fp4_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i32, vp]
     L.fp4_gemm_mx.restype = i32
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, u64, i32, u64, vp, vp, vp, vp, vp,
@@ -143,6 +146,29 @@ def fp4_hadamard_quantize_dual(x: torch.Tensor, had_n_rows: int = 32, had_rows: 
         out[0].data_ptr(), out[1].data_ptr(), had_n_cols, had_cols, sign_seed_cols & m, rnd_cols,
         sr_seed_cols & m, out[2].data_ptr(), out[3].data_ptr(), _stream_ptr(stream, dev)))
     return tuple(out)
+
+
+def fp4_wgrad_quantize(dy: torch.Tensor, x: torch.Tensor, had_n: int = 32, had: int = HAD_DET,
+                       sign_seed: int = 0, rnd: int = RTN, sr_seed_dy: int = 0, sr_seed_x: int = 0,
+                       out=None, stream=None):
+    """The Wgrad operand pair: dY[T, N] and X[T, K] quantized along T with one
+    rotation; returns (dytq, dyts, xtq, xts) (see include/fp4.h)."""
+    _need(dy, torch.bfloat16, "dy")
+    _need(x, torch.bfloat16, "x")
+    T, N = dy.shape
+    if x.shape[0] != T:
+        raise ValueError("dy and x must have the same number of rows")
+    K = x.shape[1]
+    if out is None:
+        (a, b), (c, d) = mx_shapes(T, N, AXIS_ROWS), mx_shapes(T, K, AXIS_ROWS)
+        out = tuple(torch.empty(sh, dtype=torch.uint8, device=dy.device) for sh in (a, b, c, d))
+    for t in out:
+        _need(t, torch.uint8, "output")
+    m = 2 ** 64 - 1
+    _check(lib().fp4_wgrad_quantize(dy.data_ptr(), x.data_ptr(), T, N, K, had_n, had, sign_seed & m, rnd,
+                                    sr_seed_dy & m, sr_seed_x & m, *(t.data_ptr() for t in out),
+                                    _stream_ptr(stream, dy.device)))
+    return out
 
 
 def _gemm(fn, aq, as_, bq, bs, T, N, K, out_shape, out, stream):

@@ -93,6 +93,24 @@ fp4_status fp4_hadamard_quantize_dual(const void* x_bf16, int64_t rows, int64_t 
         sr_seed_cols, codes_cols, scales_cols, (hipStream_t)stream));
 }
 
+fp4_status fp4_wgrad_quantize(const void* dy_bf16, const void* x_bf16, int64_t T, int64_t N,
+                              int64_t K, int had_n, fp4_hadamard had, uint64_t sign_seed,
+                              fp4_rounding rnd, uint64_t sr_seed_dy, uint64_t sr_seed_x,
+                              uint8_t* dytq, uint8_t* dyts, uint8_t* xtq, uint8_t* xts, void* stream) {
+    if (had != FP4_HAD_NONE && had != FP4_HAD_DET && had != FP4_HAD_SIGNED) return FP4_ERR_ENUM;
+    if (had != FP4_HAD_NONE && had_n != 16 && had_n != 32) return FP4_ERR_ENUM;
+    if (rnd != FP4_RTN && rnd != FP4_SR) return FP4_ERR_ENUM;
+    if (!dy_bf16 || !x_bf16 || !dytq || !dyts || !xtq || !xts) return FP4_ERR_NULL;
+    if (T <= 0 || N <= 0 || K <= 0 || T % 32 || !product_ok(T, N) || !product_ok(T, K))
+        return FP4_ERR_SHAPE;
+    if (!aligned16(dy_bf16) || !aligned16(x_bf16) || !aligned16(dytq) || !aligned16(dyts) ||
+        !aligned16(xtq) || !aligned16(xts))
+        return FP4_ERR_ALIGN;
+    return from_hip(fp4dev::launch_quant_mx_pair(dy_bf16, T, N, x_bf16, K, had_n, (int)had, sign_seed,
+                                                 (int)rnd, sr_seed_dy, sr_seed_x, dytq, dyts, xtq, xts,
+                                                 (hipStream_t)stream));
+}
+
 fp4_status fp4_gemm_fprop(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
                           const uint8_t* ws, int64_t T, int64_t N, int64_t K, float* y,
                           void* stream) {

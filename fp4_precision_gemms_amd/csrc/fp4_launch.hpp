@@ -21,6 +21,13 @@ hipError_t launch_quant_mx_dual(const void* x, int64_t rows, int64_t cols, int h
                                 int rnd_c, uint64_t sr_seed_c, uint8_t* codes_c, uint8_t* scales_c,
                                 hipStream_t st);
 
+// The two Wgrad operands a [rows, n1] and b [rows, n2] quantized along rows
+// with one rotation (own SR seeds), in one launch when it fits.
+hipError_t launch_quant_mx_pair(const void* a, int64_t rows, int64_t n1, const void* b, int64_t n2,
+                                int had_n, int had, uint64_t sign_seed, int rnd, uint64_t sr_a,
+                                uint64_t sr_b, uint8_t* qa, uint8_t* sa, uint8_t* qb, uint8_t* sb,
+                                hipStream_t st);
+
 // C[M, N] (row-major; fp32, or bf16 when out_bf16) = A[M, K] B[N, K]^T
 // (+ C when accumulate) over MXFP4 operands.
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,

@@ -380,20 +380,53 @@ __device__ __forceinline__ void wait_tile(int t) {
 // cols (blocks of 32 consecutive columns, rotation size HADN_C, 0 = none,
 // rounding to nearest), one (row, 32-column block) of each tile per thread,
 // read as four 16-byte LDS loads.  Needs cols % 32 == 0 then.
+//
+// A second input (x2 [rows, cols2], its own outputs and SR seed) may share
+// the launch: the grid is then 1-D, its first n_first workgroups (gx1 wide)
+// work on x and the rest (gx2 wide) on x2 -- the two Wgrad operands, same
+// rows, same rotation.
+struct RowsLdsSecond {
+    const uint16_t* x;
+    int64_t cols;
+    uint64_t sr_seed;
+    uint8_t* codes;
+    uint8_t* scales;
+    int64_t n_first, gx1, gx2;   // n_first = 0: single input, 2-D grid
+};
+
 template <int HADN, bool SR, int TB, int HADN_C>
 __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
-    uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    const uint16_t* __restrict__ x_in, int64_t rows, int64_t cols_in, uint32_t sign_word, float norm,
+    uint64_t sr_seed_in, uint8_t* __restrict__ codes_in, uint8_t* __restrict__ scales_in,
     uint32_t sign_word_c, float norm_c, uint64_t sr_seed_c, uint8_t* __restrict__ codes_c,
-    uint8_t* __restrict__ scales_c) {
+    uint8_t* __restrict__ scales_c, RowsLdsSecond second) {
     static_assert(TB == 2 || TB == 4 || TB == 8, "blocks per workgroup");
     constexpr int kTileBlocks = TB;
     __shared__ __attribute__((aligned(1024))) uint16_t tile[kTileBlocks][32 * kTileCols];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t c0 = (int64_t)__builtin_amdgcn_readfirstlane((int)blockIdx.x) * kTileCols;
+    // which input and which (column strip, row-block group) this workgroup owns
+    int64_t bx = blockIdx.x, by = blockIdx.y;
+    const uint16_t* x = x_in;
+    int64_t cols = cols_in;
+    uint64_t sr_seed = sr_seed_in;
+    uint8_t* codes = codes_in;
+    uint8_t* scales = scales_in;
+    if (second.n_first > 0) {
+        const int64_t w = blockIdx.x;
+        if (w < second.n_first) {
+            bx = w % second.gx1;
+            by = w / second.gx1;
+        } else {
+            bx = (w - second.n_first) % second.gx2;
+            by = (w - second.n_first) / second.gx2;
+            x = second.x; cols = second.cols; sr_seed = second.sr_seed;
+            codes = second.codes; scales = second.scales;
+        }
+    }
+    const int64_t c0 = (int64_t)__builtin_amdgcn_readfirstlane((int)bx) * kTileCols;
     const int64_t nrb = rows / 32;
-    const int64_t rb0 = (int64_t)__builtin_amdgcn_readfirstlane((int)blockIdx.y) * kTileBlocks;
+    const int64_t rb0 = (int64_t)__builtin_amdgcn_readfirstlane((int)by) * kTileBlocks;
     const int nt = (int)((nrb - rb0) < kTileBlocks ? (nrb - rb0) : kTileBlocks);
     // the whole input as one buffer: offsets are 32-bit, the caller bounds
     // rows * cols * 2 below 2^31; segments past the last row read as zero
@@ -547,7 +580,7 @@ hipError_t dispatch_rows_cpl(const void* x, int64_t rows, int64_t cols, uint32_t
         hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, -1>), dim3((unsigned)gx, (unsigned)gy),
                            dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
                            sr_seed, codes, scales, 0u, 1.0f, (uint64_t)0, (uint8_t*)nullptr,
-                           (uint8_t*)nullptr);
+                           (uint8_t*)nullptr, RowsLdsSecond{});
         return hipGetLastError();
     }
     if (cols % 4 == 0) return launch_rows<4, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
@@ -579,7 +612,8 @@ hipError_t launch_dual(const void* x, int64_t rows, int64_t cols, uint32_t sign_
     const int64_t gy = (rows / 32 + TB - 1) / TB;
     hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, HADN_C>), dim3((unsigned)gx, (unsigned)gy),
                        dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
-                       sr_seed, codes, scales, sign_word_c, norm_c, sr_seed_c, codes_c, scales_c);
+                       sr_seed, codes, scales, sign_word_c, norm_c, sr_seed_c, codes_c, scales_c,
+                       RowsLdsSecond{});
     return hipGetLastError();
 }
 
@@ -596,6 +630,22 @@ hipError_t dispatch_dual_c(int hadn_c, const void* x, int64_t rows, int64_t cols
                                          sign_word_c, norm_c, sr_seed_c, codes_c, scales_c, st);
     return launch_dual<HADN, SR, 32>(x, rows, cols, sign_word, norm, sr_seed, codes, scales,
                                      sign_word_c, norm_c, sr_seed_c, codes_c, scales_c, st);
+}
+
+// Both Wgrad operands (dY [rows, n1] and X [rows, n2], blocks along rows,
+// the same rotation) in one launch.
+template <int HADN, bool SR>
+hipError_t launch_pair(const void* a, int64_t rows, int64_t n1, const void* b, int64_t n2,
+                       uint32_t sign_word, float norm, uint64_t sr_a, uint64_t sr_b, uint8_t* qa,
+                       uint8_t* sa, uint8_t* qb, uint8_t* sb, hipStream_t st) {
+    constexpr int TB = kRowsLdsBlocks;
+    const int64_t gy = (rows / 32 + TB - 1) / TB;
+    const int64_t gx1 = (n1 + kTileCols - 1) / kTileCols, gx2 = (n2 + kTileCols - 1) / kTileCols;
+    const RowsLdsSecond second{(const uint16_t*)b, n2, sr_b, qb, sb, gx1 * gy, gx1, gx2};
+    hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, -1>), dim3((unsigned)((gx1 + gx2) * gy)),
+                       dim3(kTileCols), 0, st, (const uint16_t*)a, rows, n1, sign_word, norm, sr_a,
+                       qa, sa, 0u, 1.0f, (uint64_t)0, (uint8_t*)nullptr, (uint8_t*)nullptr, second);
+    return hipGetLastError();
 }
 
 // Rotation size and the binary32 factor fl(1/sqrt(n)) of a (had, had_n) pair.
@@ -653,6 +703,30 @@ hipError_t launch_quant_mx_dual(const void* x, int64_t rows, int64_t cols, int h
     if (nr == 16) FP4_DUAL(16, false);
     FP4_DUAL(32, false);
 #undef FP4_DUAL
+}
+
+hipError_t launch_quant_mx_pair(const void* a, int64_t rows, int64_t n1, const void* b, int64_t n2,
+                                int had_n, int had, uint64_t sign_seed, int rnd, uint64_t sr_a,
+                                uint64_t sr_b, uint8_t* qa, uint8_t* sa, uint8_t* qb, uint8_t* sb,
+                                hipStream_t st) {
+    if (n1 % 8 || n2 % 8 || rows * n1 * 2 >= (INT64_C(1) << 31) || rows * n2 * 2 >= (INT64_C(1) << 31) ||
+        (rows / 32) * ((n1 + 255) / 256 + (n2 + 255) / 256) >= (INT64_C(1) << 31)) {
+        // outside the fused launch's limits: one call per operand
+        const hipError_t e = launch_quant_mx(a, rows, n1, 1, had_n, had, sign_seed, rnd, sr_a, qa, sa, st);
+        if (e != hipSuccess) return e;
+        return launch_quant_mx(b, rows, n2, 1, had_n, had, sign_seed, rnd, sr_b, qb, sb, st);
+    }
+    const int n = rot_size(had, had_n);
+    const uint32_t sw = host_sign_word(had, sign_seed);
+    const float f = rot_norm(n);
+    const bool sr = rnd == 1;
+#define FP4_PAIR(HN)                                                                                 \
+    return sr ? launch_pair<HN, true>(a, rows, n1, b, n2, sw, f, sr_a, sr_b, qa, sa, qb, sb, st)    \
+              : launch_pair<HN, false>(a, rows, n1, b, n2, sw, f, sr_a, sr_b, qa, sa, qb, sb, st)
+    if (n == 0) FP4_PAIR(0);
+    if (n == 16) FP4_PAIR(16);
+    FP4_PAIR(32);
+#undef FP4_PAIR
 }
 
 hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, int had_n, int had,

@@ -152,6 +152,22 @@ fp4_status fp4_hadamard_quantize_dual(const void* x_bf16, int64_t rows, int64_t 
                                       uint8_t* codes_cols, uint8_t* scales_cols, void* stream);
 
 /*
+ * fp4_wgrad_quantize -- the two Wgrad operands in one call: exactly what
+ *   fp4_hadamard_quantize(dy, T, N, FP4_AXIS_ROWS, had_n, had, sign_seed, rnd, sr_seed_dy, dytq, dyts)
+ *   fp4_hadamard_quantize(x,  T, K, FP4_AXIS_ROWS, had_n, had, sign_seed, rnd, sr_seed_x,  xtq,  xts)
+ * write, with one launch for both when the sizes allow it.  [AMD-MXFP4,
+ * "Поисковая экспериментальная работа: корень нестабильности"]: Wgrad rotates
+ * both operands along the token axis with the same transform, so this call
+ * takes one rotation for the pair.
+ * Requirements: T % 32 == 0; pointers 16-byte aligned; the outputs must not
+ * overlap.  Errors as fp4_hadamard_quantize.
+ */
+fp4_status fp4_wgrad_quantize(const void* dy_bf16, const void* x_bf16, int64_t T, int64_t N,
+                              int64_t K, int had_n, fp4_hadamard had, uint64_t sign_seed,
+                              fp4_rounding rnd, uint64_t sr_seed_dy, uint64_t sr_seed_x,
+                              uint8_t* dytq, uint8_t* dyts, uint8_t* xtq, uint8_t* xts, void* stream);
+
+/*
  * The three scaled-FP4 GEMMs of a linear layer.  [AMD-MXFP4, "Поисковая
  * экспериментальная работа: корень нестабильности"]: Fprop Y = X W^T,
  * Dgrad dX = dY W, Wgrad dW = dY^T X, all in MXFP4 on native FP4 matrix

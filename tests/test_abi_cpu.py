@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp4_hadamard_quantize", "fp4_gemm_fprop", "fp4_gemm_dgrad", "fp4_gemm_wgrad",
-              "fp4_gemm_mx", "fp4_hadamard_quantize_dual", "nvfp4_quantize",
+              "fp4_gemm_mx", "fp4_hadamard_quantize_dual", "fp4_wgrad_quantize", "nvfp4_quantize",
               "nvfp4_workspace_bytes", "fp4_status_string"):
         assert n in names
 
@@ -125,6 +125,21 @@ def test_quantize_dual_errors(L):
     assert call(rows=0) == ERR_SHAPE
     assert call(ptrs=(A, A, MIS, A)) == ERR_ALIGN
     assert call(x=MIS) == ERR_ALIGN
+
+
+def test_wgrad_quantize_errors(L):
+    def call(T=64, N=64, K=64, hn=32, had=1, rnd=0, p=(A, A, A, A, A, A)):
+        return L.fp4_wgrad_quantize(p[0], p[1], T, N, K, hn, had, 0, rnd, 0, 0, p[2], p[3], p[4], p[5], None)
+
+    assert call(had=3) == ERR_ENUM
+    assert call(hn=8) == ERR_ENUM
+    assert call(rnd=2) == ERR_ENUM
+    assert call(p=(A, None, A, A, A, A)) == ERR_NULL
+    assert call(p=(A, A, A, A, A, None)) == ERR_NULL
+    assert call(T=48) == ERR_SHAPE
+    assert call(K=0) == ERR_SHAPE
+    assert call(N=-1) == ERR_SHAPE
+    assert call(p=(A, A, A, MIS, A, A)) == ERR_ALIGN
 
 
 def test_gemm_mx_errors(L):
