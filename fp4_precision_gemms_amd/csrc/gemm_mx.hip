@@ -419,98 +419,80 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
         // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
-        // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.
+        // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.  The wave's rows
+        // go out through LDS: the stage buffers are free once every wave is
+        // past its last fragment read; each wave stages up to 32 KB of its
+        // tile at a time in its own quarter of them (rows padded by 16 bytes:
+        // conflict-free writes of the accumulator layout and row reads), then
+        // reads back four consecutive n of a row per lane, TN / 4 lanes per
+        // row, so that a store instruction covers whole rows of the tile.
+        // fp32 rows are whole 128-byte lines, written non-temporally; with
+        // N % 4 != 0 (rows not 16-byte aligned) elements go one by one.
         const bool vec_store = (N % 4) == 0;
-        // fp32 overwrite with N % 4 == 0: the wave's rows go out through LDS
-        // in whole 128-byte lines (TN / 4 lanes per row), so every store
-        // instruction writes full lines.  The stage buffers are free once
-        // every wave is past its last fragment read; each wave stages up to
-        // 32 KB of its tile at a time in its own quarter of them, rows
-        // padded by 16 bytes (conflict-free writes of the accumulator
-        // layout, conflict-free row reads).
         constexpr int kRowBytes = TN * 4 + 16;
-        constexpr int kLanesPerRow = TN / 4, kRowsPerInst = 64 / kLanesPerRow;
-        constexpr bool kStaged = !OBF16 && !ACC && (64 % kLanesPerRow == 0) && (32 * kRowBytes <= 32768) &&
-                                 (NW == 4) && (kStage >= 65536);
-        if constexpr (kStaged) {
-            if (vec_store) {
-                constexpr int ICH = (32768 / kRowBytes) / 32 < FM ? (32768 / kRowBytes) / 32 : FM;
-                uint8_t* const reg = ((wave >> 1) ? lds1 : lds0) + (wave & 1) * 32768;
-                __syncthreads();                        // all fragment reads of the tile are done
+        constexpr int kLanesPerRow = TN / 4;
+        constexpr int kRowsPerInst = kLanesPerRow >= 64 ? 1 : 64 / kLanesPerRow;
+        static_assert(NW == 4 && kStage >= 65536 && 32 * kRowBytes <= 32768 && kLanesPerRow <= 64,
+                      "each wave stages at least 32 rows of its tile in 32 KB");
+        constexpr int ICH = (32768 / kRowBytes) / 32 < FM ? (32768 / kRowBytes) / 32 : FM;
+        uint8_t* const reg = ((wave >> 1) ? lds1 : lds0) + (wave & 1) * 32768;
+        __syncthreads();                                // all fragment reads of the tile are done
     #pragma unroll
-                for (int i0 = 0; i0 < FM; i0 += ICH) {
+        for (int i0 = 0; i0 < FM; i0 += ICH) {
     #pragma unroll
-                    for (int ii = 0; ii < ICH; ++ii) {
-                        if (i0 + ii >= FM) break;
+            for (int ii = 0; ii < ICH; ++ii) {
+                if (i0 + ii >= FM) break;
     #pragma unroll
-                        for (int j = 0; j < FN; ++j)
+                for (int j = 0; j < FN; ++j)
     #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const int row = ii * 32 + l32, cn = j * 32 + 8 * q + 4 * h;
-                                *reinterpret_cast<float4*>(reg + row * kRowBytes + cn * 4) =
-                                    make_float4(acc[i0 + ii][j][4 * q], acc[i0 + ii][j][4 * q + 1],
-                                                acc[i0 + ii][j][4 * q + 2], acc[i0 + ii][j][4 * q + 3]);
-                            }
+                    for (int q = 0; q < 4; ++q) {
+                        const int row = ii * 32 + l32, cn = j * 32 + 8 * q + 4 * h;
+                        *reinterpret_cast<float4*>(reg + row * kRowBytes + cn * 4) =
+                            make_float4(acc[i0 + ii][j][4 * q], acc[i0 + ii][j][4 * q + 1],
+                                        acc[i0 + ii][j][4 * q + 2], acc[i0 + ii][j][4 * q + 3]);
                     }
-                    const int nrows = (FM - i0 < ICH ? FM - i0 : ICH) * 32;
-    #pragma unroll
-                    for (int rr = 0; rr < ICH * 32; rr += kRowsPerInst) {
-                        const int row = rr + lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
-                        if (rr >= nrows) break;
-                        const float4 v = *reinterpret_cast<const float4*>(reg + row * kRowBytes + c4 * 4);
-                        const int64_t m = m0 + wm * TM + i0 * 32 + row, n = n0 + wn * TN + c4;
-                        if (m < M && n + 4 <= N)
-                            store_c_line_part(reinterpret_cast<float*>(C) + m * N + n, v);
-                    }
-                }
-                continue;                               // next tile
             }
-        }
-        // Each (i, j, q) is four consecutive n of one row: one 16-byte fp32
-        // or 8-byte bf16 access when N % 4 == 0 and all four exist.
+            const int nrows = (FM - i0 < ICH ? FM - i0 : ICH) * 32;
+            const int lr = lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
+            const bool lane_on = lr < kRowsPerInst;
     #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t m = m0 + wm * TM + i * 32 + l32;
-            if (m >= M) continue;
-    #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-    #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n0 + wn * TN + j * 32 + 8 * q + 4 * h;
-                    float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                  acc[i][j][4 * q + 3]};
-                    if constexpr (OBF16) {
-                        uint16_t* crow = reinterpret_cast<uint16_t*>(C) + m * N;
-                        if (vec_store && n + 4 <= N) {
-                            uint2* p = reinterpret_cast<uint2*>(crow + n);
-                            if constexpr (ACC) {
-                                const uint2 o = *p;
-                                v[0] += bf16_value(o.x & 0xFFFFu); v[1] += bf16_value(o.x >> 16);
-                                v[2] += bf16_value(o.y & 0xFFFFu); v[3] += bf16_value(o.y >> 16);
-                            }
-                            *p = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                                            bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
-                        } else {
-                            for (int e = 0; e < 4; ++e) {
-                                if (n + e >= N) break;
-                                const float old = ACC ? bf16_value(crow[n + e]) : 0.0f;
-                                crow[n + e] = (uint16_t)bf16_rne(ACC ? v[e] + old : v[e]);
-                            }
+            for (int rr = 0; rr < ICH * 32; rr += kRowsPerInst) {
+                if (rr >= nrows) break;
+                const int row = rr + lr;
+                const float4 f = *reinterpret_cast<const float4*>(reg + (lane_on ? row : 0) * kRowBytes + c4 * 4);
+                const int64_t m = m0 + wm * TM + i0 * 32 + row, n = n0 + wn * TN + c4;
+                if (!lane_on || m >= M) continue;
+                float v[4] = {f.x, f.y, f.z, f.w};
+                if constexpr (OBF16) {
+                    uint16_t* crow = reinterpret_cast<uint16_t*>(C) + m * N;
+                    if (vec_store && n + 4 <= N) {
+                        uint2* p = reinterpret_cast<uint2*>(crow + n);
+                        if constexpr (ACC) {
+                            const uint2 o = *p;
+                            v[0] += bf16_value(o.x & 0xFFFFu); v[1] += bf16_value(o.x >> 16);
+                            v[2] += bf16_value(o.y & 0xFFFFu); v[3] += bf16_value(o.y >> 16);
                         }
+                        *p = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                        bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
                     } else {
-                        float* crow = reinterpret_cast<float*>(C) + m * N;
-                        if (vec_store && n + 4 <= N) {
-                            float4* p = reinterpret_cast<float4*>(crow + n);
-                            if constexpr (ACC) {
-                                const float4 o = *p;
-                                v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-                            }
-                            *p = make_float4(v[0], v[1], v[2], v[3]);
-                        } else {
-                            for (int e = 0; e < 4; ++e) {
-                                if (n + e >= N) break;
-                                crow[n + e] = ACC ? v[e] + crow[n + e] : v[e];
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            if (n + e >= N) break;
+                            const float old = ACC ? bf16_value(crow[n + e]) : 0.0f;
+                            crow[n + e] = (uint16_t)bf16_rne(ACC ? v[e] + old : v[e]);
+                        }
+                    }
+                } else {
+                    float* crow = reinterpret_cast<float*>(C) + m * N;
+                    if (vec_store && n + 4 <= N) {
+                        if constexpr (ACC) {
+                            const float4 o = *reinterpret_cast<const float4*>(crow + n);
+                            v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+                        }
+                        store_c_line_part(crow + n, make_float4(v[0], v[1], v[2], v[3]));
+                    } else {
+                        for (int e = 0; e < 4; ++e) {
+                            if (n + e >= N) break;
+                            crow[n + e] = ACC ? v[e] + crow[n + e] : v[e];
                         }
                     }
                 }
