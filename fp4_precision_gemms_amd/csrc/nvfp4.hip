@@ -17,7 +17,10 @@
 //               float bits, valid because every value is non-negative);
 //   nv_quant -- rotate again, derive s_t from the amax, per block the E4M3
 //               scale, the E2M1 codes and, with renorm, the scale rounded
-//               stochastically toward |y|^2 / (s_t sum y_i q_i).
+//               stochastically toward |y|^2 / (s_t sum y_i q_i).  The codes
+//               come from the hardware FP4 conversion of fl(y_i * inv) with
+//               scale 1 (round to nearest even, saturating -- the rule the
+//               MX quantizers check bit-exact), q_i from its inverse.
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
@@ -25,6 +28,13 @@ namespace fp4dev {
 namespace {
 
 constexpr int kThreads = 256;
+// 16-byte chunks per thread: in nv_quant the upper halves (or lower) of 4
+// consecutive 16-element blocks, so one Philox call gives the 4 blocks'
+// scale SR words; in nv_amax 4 independent loads in flight.
+constexpr int kUnroll = 4;
+// Workgroups of the amax pass (each ends with one atomic max on the same
+// word: 8192 of them serialized behind each other cost 2x the pass).
+constexpr int64_t kAmaxBlocks = 1024;
 
 __device__ __forceinline__ float pair_xor1f(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -72,12 +82,21 @@ __global__ __launch_bounds__(kThreads) void nv_amax(const uint4* __restrict__ x,
     __shared__ uint32_t red[kThreads / 64];
     uint32_t m = 0;
     const int q = threadIdx.x & 1;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nchunks; g += stride) {
-        float a[8];
-        load_rotate8<HAD>(x[g], q, sign_word, a);
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
+    for (int64_t g0 = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; g0 < nchunks; g0 += stride) {
+        uint4 w[kUnroll];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(a[t]) & 0x7FFFFFFFu);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t g = g0 + (int64_t)u * kThreads;
+            w[u] = g < nchunks ? x[g] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float a[8];
+            load_rotate8<HAD>(w[u], q, sign_word, a);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(a[t]) & 0x7FFFFFFFu);
+        }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
@@ -91,10 +110,29 @@ __global__ __launch_bounds__(kThreads) void nv_amax(const uint4* __restrict__ x,
     }
 }
 
-__device__ __forceinline__ float e2m1_signed_value(uint32_t code) {
-    const uint32_t m = code & 7u, e = m >> 1, mb = m & 1u;
-    const uint32_t mag = e == 0u ? (mb ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (mb << 22));
-    return __uint_as_float(mag | ((code & 8u) << 28));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// E2M1 codes of 8 binary32 values, nearest with ties to even, saturating at
+// 6: V_CVT_SCALEF32_PK_FP4_F32 with scale 1 -- the same rounding as the MX
+// quantizers' hardware path (there checked bit-exact against the integer
+// encoder for power-of-two scales, 1 among them); two values per
+// instruction, the first in the low nibble.
+__device__ __forceinline__ uint32_t encode8_unit(const float* v) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+    return w;
+}
+
+// The 8 E2M1 values of a code word (exact; low nibble first).
+__device__ __forceinline__ void decode8(uint32_t w, float* out) {
+    v2f r;
+    r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); out[0] = r.x; out[1] = r.y;
+    r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); out[2] = r.x; out[3] = r.y;
+    r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); out[4] = r.x; out[5] = r.y;
+    r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); out[6] = r.x; out[7] = r.y;
 }
 
 template <bool HAD, bool RENORM>
@@ -105,55 +143,74 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
     const float amax = *amax_p;
     const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;   // 6 * 448
     const float six_st = 6.0f * s_t;
-    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (g == 0) *tensor_scale = s_t;
-    if (g >= nchunks) return;                                   // uniform per pair
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
     const int q = threadIdx.x & 1;
-    float y[8];
-    load_rotate8<HAD>(x[g], q, sign_word, y);
-    uint32_t m = 0;
+    // With renorm, lane pair p (lanes 2p, 2p+1 of the grid) owns blocks
+    // 4p .. 4p+3, one 8-element half of each per lane (chunk 2 blk + q), so
+    // that one Philox call serves all four; without, chunk u of a thread is
+    // kThreads chunks after chunk u - 1 (every load instruction contiguous).
+    // All chunks are loaded first.
+    const int64_t pair = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 1;
+    auto chunk = [&](int u) -> int64_t {
+        return RENORM ? 8 * pair + 2 * u + q : ((int64_t)blockIdx.x * kUnroll + u) * kThreads + threadIdx.x;
+    };
+    uint4 wv[kUnroll];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(y[t]) & 0x7FFFFFFFu);
-    m = max(m, pair_xor1(m));
-    const uint32_t sb = e4m3_rne(__uint_as_float(m) / six_st);
-    uint32_t word = 0, stored = sb;
-    if (sb != 0u) {
-        const float inv = 1.0f / (e4m3_value(sb) * s_t);
-        uint32_t cq[8];
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t g = chunk(u);
+        wv[u] = g < nchunks ? x[g] : make_uint4(0, 0, 0, 0);
+    }
+    // scale SR words of the 4 blocks: word u of counter (blk >> 2) = p
+    uint4 srw = make_uint4(0, 0, 0, 0);
+    if constexpr (RENORM) srw = stream4(sr_seed, 2u, (uint64_t)pair);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            cq[t] = e2m1_rtn(y[t] * inv);
-            word |= cq[t] << (4 * t);
-        }
-        if constexpr (RENORM) {
-            // sequential binary32 fmaf chains over the 16 elements in order:
-            // the lower lane's partial sums seed the upper lane's chain
-            float num = 0.0f, den = 0.0f;
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t g = chunk(u);
+        if (g >= nchunks) break;                                    // uniform per pair
+        float y[8];
+        load_rotate8<HAD>(wv[u], q, sign_word, y);
+        uint32_t m = 0;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                num = fmaf(y[t], y[t], num);
-                den = fmaf(y[t], e2m1_signed_value(cq[t]), den);
-            }
-            float pnum = pair_xor1f(num), pden = pair_xor1f(den);
-            if (q) {
-                num = pnum;
-                den = pden;
+        for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(y[t]) & 0x7FFFFFFFu);
+        m = max(m, pair_xor1(m));
+        const uint32_t sb = e4m3_rne(__uint_as_float(m) / six_st);
+        uint32_t word = 0, stored = sb;
+        if (sb != 0u) {
+            const float inv = 1.0f / (e4m3_value(sb) * s_t);
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = y[t] * inv;
+            word = encode8_unit(v);
+            if constexpr (RENORM) {
+                // sequential binary32 fmaf chains over the 16 elements in order:
+                // the lower lane's partial sums seed the upper lane's chain
+                float yq[8];
+                decode8(word, yq);
+                float num = 0.0f, den = 0.0f;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     num = fmaf(y[t], y[t], num);
-                    den = fmaf(y[t], e2m1_signed_value(cq[t]), den);
+                    den = fmaf(y[t], yq[t], den);
                 }
-                if (den > 0.0f) {
-                    const float target = num / (s_t * den);
-                    const uint64_t blk = (uint64_t)g >> 1;
-                    const uint32_t u = word_of(stream4(sr_seed, 2u, blk >> 2), (int)(blk & 3));
-                    stored = e4m3_sr(target, u);
+                float pnum = pair_xor1f(num), pden = pair_xor1f(den);
+                if (q) {
+                    num = pnum;
+                    den = pden;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        num = fmaf(y[t], y[t], num);
+                        den = fmaf(y[t], yq[t], den);
+                    }
+                    if (den > 0.0f) {
+                        const float target = num / (s_t * den);
+                        stored = e4m3_sr(target, word_of(srw, u));
+                    }
                 }
             }
         }
+        codes[g] = word;
+        if (q == 1) scales[g >> 1] = (uint8_t)stored;
     }
-    codes[g] = word;
-    if (q == 1) scales[g >> 1] = (uint8_t)stored;
 }
 
 template <bool HAD>
@@ -165,13 +222,13 @@ hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw,
     if (!amax_p) {
         uint32_t* ws = (uint32_t*)workspace;
         hipLaunchKernelGGL(nv_clear, dim3(1), dim3(64), 0, st, ws);
-        int64_t blocks = (nchunks + kThreads - 1) / kThreads;
-        if (blocks > 8192) blocks = 8192;
+        int64_t blocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+        if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
         hipLaunchKernelGGL((nv_amax<HAD>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
                            (const uint4*)x, nchunks, sw, ws);
         amax_p = (const float*)ws;
     }
-    const int64_t qblocks = (nchunks + kThreads - 1) / kThreads;
+    const int64_t qblocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
     if (renorm) {
         hipLaunchKernelGGL((nv_quant<HAD, true>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
                            (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
