@@ -11,6 +11,7 @@ are synthetic bf16 tensors resident in HBM before timing starts.
     python bench.py [--steps K] [--warmup W] [--workload gate_up] [--no-cpu-baseline]
                     [--copy-calibration]
     python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
+    python bench.py --nvfp4                            (the secondary NVFP4 quantizer)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
 (2 T N K flops over the whole step); the roofline object describes the
@@ -149,6 +150,61 @@ def cpu_baseline(w, dY, X):
                       % (w.T, w.N, w.T, w.K, t1 - t0, n, w.N, t2 - t1, t_full)}
 
 
+def nvfp4_bench(args) -> int:
+    """The secondary kernel: NVFP4 quantization of the [16384 x 8192]
+    Student-t (nu = 4) tensor with the random-sign Hadamard-16 and the renorm
+    folded into the E4M3 scales by SR, the tensor amax computed in-library
+    (two passes) and supplied (one pass).  One JSON line; HBM roofline over
+    algorithmic bytes (2.5625 B/element, +2 B/element for the amax pass)."""
+    import numpy as np
+    import torch
+
+    import fp4_precision_gemms_amd as F
+    import workloads as W
+
+    w = W.WORKLOADS["nvfp4"]
+    rows, cols = w.T, w.K
+    dev = torch.device("cuda:0")
+    bits = W.tensor(w, "x")
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(F.nvfp4_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    F.nvfp4_quantize(x, F.HAD_SIGNED, 7, 1, 11, codes=codes, scales=scales, tensor_scale=ts,
+                     workspace=ws)
+    amax = (ts * 2688.0).contiguous()          # the amax the first call found, for the one-pass run
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / args.steps
+
+    el = rows * cols
+    t2 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, 1, 11, codes=codes, scales=scales,
+                                        tensor_scale=ts, workspace=ws))
+    t1 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, 1, 11, amax_in=amax, codes=codes,
+                                        scales=scales, tensor_scale=ts))
+    b1, b2 = el * (2 + 0.5 + 1 / 16), el * (2 + 0.5 + 1 / 16 + 2)
+    g2, g1 = b2 / (t2 * 1e-3) / 1e9, b1 / (t1 * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "NVFP4 quantize GB/s (16384x8192, SIGNED-16, renorm by SR, amax in-library)",
+        "value": g2, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t2, "higher_is_better": True, "dtype": "bf16->nvfp4", "data": "synthetic",
+        "config": {"workload": "nvfp4 [16384x8192] Student-t nu=4", "had": "signed-16", "renorm": 1},
+        "roofline": {"bound": "hbm", "achieved": g2, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": g2 / HBM_PEAK_GBS, "traffic": None},
+        "one_pass_amax_in": {"ms": t1, "GBps": g1, "frac_hbm": g1 / HBM_PEAK_GBS}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +218,7 @@ def main() -> int:
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 counter runs and exit")
+    ap.add_argument("--nvfp4", action="store_true", help="time the NVFP4 quantizer instead")
     args = ap.parse_args()
     if args.counters:
         return counter_summary(*args.counters)
@@ -169,6 +226,9 @@ def main() -> int:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
+
+    if args.nvfp4:
+        return nvfp4_bench(args)
 
     import numpy as np
     import torch
