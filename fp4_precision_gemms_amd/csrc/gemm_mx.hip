@@ -189,27 +189,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
     // one workgroup per CU, so consecutive tile indices still land on the
     // XCDs round-robin).
     const int ntiles = tiles_m * tiles_n;
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        // every wave is done with the previous tile's LDS before it is refilled
-        if (t != (int)blockIdx.x) {
-            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-            barrier_after_wait();
-        }
+    const int64_t kbytes = K / 2, ks = K / 32;
+    const int nk = (int)((K + BK - 1) / BK);
+    // The current tile: origin and buffer views of its rows (rows past M / N
+    // are out of range).  Set before the tile's first DMA, which for all but
+    // a workgroup's first tile may be issued during the previous tile's
+    // epilogue.
+    int64_t m0 = 0, n0 = 0, rows_a = 0, rows_b = 0;
+    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferWord3);
+    __amdgpu_buffer_rsrc_t rb = ra;
+    auto set_tile = [&](int t) {
         int tile_m, tile_n;
         tile_of_block<GM>(t, ntiles, tiles_m, tiles_n, tile_m, tile_n);
         tile_m = __builtin_amdgcn_readfirstlane(tile_m);
         tile_n = __builtin_amdgcn_readfirstlane(tile_n);
-        const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-        const int64_t kbytes = K / 2, ks = K / 32;
-        const int nk = (int)((K + BK - 1) / BK);
-
-        // Buffer views of this block's rows: rows past M / N are out of range.
-        const int64_t rows_a = (M - m0) < BM ? (M - m0) : BM;
-        const int64_t rows_b = (N - n0) < BN ? (N - n0) : BN;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(A + m0 * kbytes), (short)0, (int)(rows_a * kbytes), kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(B + n0 * kbytes), (short)0, (int)(rows_b * kbytes), kBufferWord3);
+        m0 = (int64_t)tile_m * BM;
+        n0 = (int64_t)tile_n * BN;
+        rows_a = (M - m0) < BM ? (M - m0) : BM;
+        rows_b = (N - n0) < BN ? (N - n0) : BN;
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * kbytes), (short)0, (int)(rows_a * kbytes),
+                                               kBufferWord3);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * kbytes), (short)0, (int)(rows_b * kbytes),
+                                               kBufferWord3);
+    };
+    // Epilogue staging: with kEarly each wave stages its rows in a quarter of
+    // stage buffer 1 only, so the next tile's first stage can land in stage
+    // buffer 0 meanwhile; otherwise in 32 KB spread over both buffers.
+    constexpr int kRowBytes = TN * 4 + 16;
+    constexpr int kLanesPerRow = TN / 4;
+    constexpr int kRowsPerInst = kLanesPerRow >= 64 ? 1 : 64 / kLanesPerRow;
+    constexpr bool kEarly = !KTAIL && !ACC && NBUF == 2 && 32 * kRowBytes <= kStage / 4 &&
+                            kRowsPerInst * kLanesPerRow == 64;
+    constexpr int kRegion = kEarly ? kStage / 4 / 16 * 16 : 32768;
+    // store instructions of a full tile's epilogue (they follow the next
+    // tile's first DMA in the wave's memory counter)
+    constexpr int kEpiStores = FM * 32 / kRowsPerInst;
+    bool early = false;   // this tile's first stage was issued during the previous epilogue
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        if (!early) {
+            // every wave is done with the previous tile's LDS before it is refilled
+            if (t != (int)blockIdx.x) {
+                __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+                barrier_after_wait();
+            }
+            set_tile(t);
+        }
 
         // Per-lane DMA offsets within the stage at k = 0; the stage's k offset
         // goes in the scalar offset.  Codes: row lane / CPR of an RPI-row group,
@@ -396,10 +420,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
 
         uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
         const int kfirst = -((NBUF - nk % NBUF) % NBUF);
+        if (!early) {
     #pragma unroll
-        for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
-        if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-        else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
+            for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
+            if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+            else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
+        } else {
+            // the first stage went out before the previous tile's kEpiStores
+            // stores (the memory counter completes in order)
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kEpiStores < 63 ? kEpiStores : 63));
+        }
         barrier_after_wait();
         Scales sc0, sc1;
         read_scales(bufs[0], sc0);
@@ -417,26 +447,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
         // the prefetches past the last stage must land before the workgroup
         // (and its LDS) goes away
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        __syncthreads();                                // all fragment reads of the tile are done
+        const int64_t em0 = m0, en0 = n0;               // the tile the epilogue writes
+        const bool vec_store = (N % 4) == 0;
+        const bool full_tile = vec_store && em0 + BM <= M && en0 + BN <= N;   // workgroup-uniform
+        early = false;
+        if constexpr (kEarly) {
+            // The next tile's first stage goes out now, into stage buffer 0
+            // (this epilogue stages in buffer 1 only); it is waited for at
+            // the start of the next tile.
+            const int tn = t + (int)gridDim.x;
+            if (full_tile && tn < ntiles) {
+                set_tile(tn);
+    #pragma unroll
+                for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
+                early = true;
+            }
+        }
 
         // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
         // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.  The wave's rows
         // go out through LDS: the stage buffers are free once every wave is
-        // past its last fragment read; each wave stages up to 32 KB of its
-        // tile at a time in its own quarter of them (rows padded by 16 bytes:
+        // past its last fragment read; each wave stages a few 32-row pieces of
+        // its tile at a time in its own region (rows padded by 16 bytes:
         // conflict-free writes of the accumulator layout and row reads), then
         // reads back four consecutive n of a row per lane, TN / 4 lanes per
         // row, so that a store instruction covers whole rows of the tile.
         // fp32 rows are whole 128-byte lines, written non-temporally; with
         // N % 4 != 0 (rows not 16-byte aligned) elements go one by one.
-        const bool vec_store = (N % 4) == 0;
-        constexpr int kRowBytes = TN * 4 + 16;
-        constexpr int kLanesPerRow = TN / 4;
-        constexpr int kRowsPerInst = kLanesPerRow >= 64 ? 1 : 64 / kLanesPerRow;
-        static_assert(NW == 4 && kStage >= 65536 && 32 * kRowBytes <= 32768 && kLanesPerRow <= 64,
-                      "each wave stages at least 32 rows of its tile in 32 KB");
-        constexpr int ICH = (32768 / kRowBytes) / 32 < FM ? (32768 / kRowBytes) / 32 : FM;
-        uint8_t* const reg = ((wave >> 1) ? lds1 : lds0) + (wave & 1) * 32768;
-        __syncthreads();                                // all fragment reads of the tile are done
+        static_assert(NW == 4 && kStage >= 65536 && 32 * kRowBytes <= kRegion && kLanesPerRow <= 64,
+                      "each wave stages at least 32 rows of its tile");
+        constexpr int ICH = (kRegion / kRowBytes) / 32 < FM ? (kRegion / kRowBytes) / 32 : FM;
+        uint8_t* const reg = kEarly ? lds1 + wave * kRegion : ((wave >> 1) ? lds1 : lds0) + (wave & 1) * 32768;
     #pragma unroll
         for (int i0 = 0; i0 < FM; i0 += ICH) {
     #pragma unroll
@@ -455,12 +497,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
             const int nrows = (FM - i0 < ICH ? FM - i0 : ICH) * 32;
             const int lr = lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
             const bool lane_on = lr < kRowsPerInst;
+            if (full_tile) {
+                // every row and column in range: batches of kBatch row
+                // reads go out back to back, then their stores
+                constexpr int kBatch = 8;
+    #pragma unroll
+                for (int rb = 0; rb < ICH * 32; rb += kBatch * kRowsPerInst) {
+                    if (rb >= nrows) break;
+                    float4 f[kBatch];
+    #pragma unroll
+                    for (int k = 0; k < kBatch; ++k)
+                        f[k] = *reinterpret_cast<const float4*>(
+                            reg + (lane_on ? rb + k * kRowsPerInst + lr : 0) * kRowBytes + c4 * 4);
+                    if (lane_on) {
+    #pragma unroll
+                        for (int k = 0; k < kBatch; ++k) {
+                            const int64_t m = em0 + wm * TM + i0 * 32 + rb + k * kRowsPerInst + lr;
+                            const int64_t n = en0 + wn * TN + c4;
+                            float v[4] = {f[k].x, f[k].y, f[k].z, f[k].w};
+                            if constexpr (OBF16) {
+                                uint2* p = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + m * N + n);
+                                if constexpr (ACC) {
+                                    const uint2 o = *p;
+                                    v[0] += bf16_value(o.x & 0xFFFFu); v[1] += bf16_value(o.x >> 16);
+                                    v[2] += bf16_value(o.y & 0xFFFFu); v[3] += bf16_value(o.y >> 16);
+                                }
+                                *p = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                                bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+                            } else {
+                                float* p = reinterpret_cast<float*>(C) + m * N + n;
+                                if constexpr (ACC) {
+                                    const float4 o = *reinterpret_cast<const float4*>(p);
+                                    v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+                                }
+                                store_c_line_part(p, make_float4(v[0], v[1], v[2], v[3]));
+                            }
+                        }
+                    }
+                }
+                continue;
+            }
     #pragma unroll
             for (int rr = 0; rr < ICH * 32; rr += kRowsPerInst) {
                 if (rr >= nrows) break;
                 const int row = rr + lr;
                 const float4 f = *reinterpret_cast<const float4*>(reg + (lane_on ? row : 0) * kRowBytes + c4 * 4);
-                const int64_t m = m0 + wm * TM + i0 * 32 + row, n = n0 + wn * TN + c4;
+                const int64_t m = em0 + wm * TM + i0 * 32 + row, n = en0 + wn * TN + c4;
                 if (!lane_on || m >= M) continue;
                 float v[4] = {f.x, f.y, f.z, f.w};
                 if constexpr (OBF16) {

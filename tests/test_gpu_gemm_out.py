@@ -108,3 +108,43 @@ def test_role_entry_points_equal_gemm_mx():
     b = F.fp4_gemm_mx(*g)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# More tiles than compute units, so each persistent workgroup runs several
+# tiles: the tile-to-tile hand-over (the next tile's first stage issued during
+# the current tile's epilogue, when both are full) with every tile shape and
+# output mode.  (14336, 4096): 1024 full 224 x 256 tiles; (14300, 4000):
+# ragged last tile row and column; (4096, 14336): 256 x 224 tiles;
+# (8192, 8192): 256 x 256 tiles.
+MULTI_TILE = [(14336, 4096, 512), (14300, 4000, 512), (4096, 14336, 512), (8192, 8192, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", MULTI_TILE)
+@pytest.mark.parametrize("mode", ["f32", "bf16", "f32_acc"])
+def test_multi_tile_sampled(M, N, K, mode):
+    rng, aq, as_, bq, bs = operands(M, N, K, M + 3 * N + K)
+    say("gemm_mx multi-tile", mode, M, N, K)
+    need_gpu()
+    if mode == "bf16":
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    elif mode == "f32":
+        out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        c_old = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).cuda()
+        out = c_old.clone()
+    got = run(aq, as_, bq, bs, out, F.OUT_BF16 if mode == "bf16" else F.OUT_F32, mode == "f32_acc")
+    # whole rows and columns at tile edges and in the middle, then random
+    rows = [0, 223, 224, 255, 256, M // 2 + 17, M - 1]
+    cols = [0, 223, 224, 255, 256, N // 2 + 5, N - 1]
+    mi = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, 4000)])
+    ni = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, 4000)])
+    ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
+    g = got[mi, ni]
+    if mode == "bf16":
+        bf16_check(g, ref, mag)
+    elif mode == "f32":
+        gemm_check(g, ref, mag, TOL)
+    else:
+        old = c_old.cpu().numpy()[mi, ni].astype(np.float64)
+        gemm_check(g, ref + old, mag + np.abs(old), TOL)
+    assert np.isfinite(got).all()
