@@ -238,8 +238,12 @@ def nvfp4_amax(x, had=HAD_SIGNED, sign_seed=0) -> np.float32:
     return np.float32(lib().oracle_nvfp4_amax(x, x.shape[0], x.shape[1], had, sign_seed))
 
 
-def nvfp4_quantize(x, had=HAD_SIGNED, sign_seed=0, renorm=1, sr_seed=0, amax_in=None):
-    """NVFP4 codes [rows, cols/2], E4M3 scales [rows, cols/16], tensor scale."""
+NV_RTN, NV_RENORM_SR, NV_ELEMENT_SR = 0, 1, 2
+
+
+def nvfp4_quantize(x, had=HAD_SIGNED, sign_seed=0, mode=NV_RENORM_SR, sr_seed=0, amax_in=None):
+    """NVFP4 codes [rows, cols/2], E4M3 scales [rows, cols/16], tensor scale.
+    mode: NV_RTN, NV_RENORM_SR (renormalized scales by SR) or NV_ELEMENT_SR."""
     x = _bits16(x)
     rows, cols = x.shape
     codes = np.zeros((rows, cols // 2), dtype=np.uint8)
@@ -249,7 +253,7 @@ def nvfp4_quantize(x, had=HAD_SIGNED, sign_seed=0, renorm=1, sr_seed=0, amax_in=
     if amax_in is not None:
         amax_buf = ctypes.c_float(float(amax_in))
         amax_ptr = ctypes.cast(ctypes.pointer(amax_buf), ctypes.c_void_p)
-    rc = lib().oracle_nvfp4_quantize(x, rows, cols, had, sign_seed, renorm, sr_seed,
+    rc = lib().oracle_nvfp4_quantize(x, rows, cols, had, sign_seed, mode, sr_seed,
                                      amax_ptr, codes, scales, ctypes.byref(ts))
     if rc:
         raise ValueError("oracle_nvfp4_quantize rejected its arguments")

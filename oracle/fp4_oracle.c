@@ -458,15 +458,22 @@ float oracle_nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int had,
  *     the stored scale is SR(s_b * rho) = SR(|y|^2 / (s_t * sum y_i q_i)) onto
  *     E4M3 with the purpose-2 stream at the block index; sums are binary32
  *     fmaf chains in element order.  A block with sum y_i q_i <= 0 keeps s_b.
+ * mode: 0 = elements to nearest, scale s_b; 1 = elements to nearest, scale
+ * renormalized as above; 2 = every element rounded stochastically instead
+ * ([QUARTET-II]: the recipe it compares against rounds each FP4 element
+ * stochastically; [NV-NVFP4, "Как это работает"]: stochastic rounding in the
+ * computations), scale s_b.  Reading for mode 2: the E2M1 stochastic
+ * rounding of oracle_e2m1_sr with the purpose-0 stream at the element's
+ * row-major index r * cols + c, the same stream as MXFP4's SR.
  * amax_in (nullable) replaces the computed tensor amax.
  * codes[rows, cols/2], scales[rows, cols/16] (E4M3 bytes), *tensor_scale. */
 int oracle_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int had,
-                          uint64_t sign_seed, int renorm, uint64_t sr_seed,
+                          uint64_t sign_seed, int mode, uint64_t sr_seed,
                           const float* amax_in, uint8_t* codes, uint8_t* scales,
                           float* tensor_scale) {
     if (rows <= 0 || cols <= 0 || cols % 16) return 1;
     if (had != HAD_NONE && had != HAD_DET && had != HAD_SIGNED) return 1;
-    if (renorm != 0 && renorm != 1) return 1;
+    if (mode != 0 && mode != 1 && mode != 2) return 1;
     float signs[16];
     if (had != HAD_NONE) oracle_hadamard_signs(had, 16, sign_seed, signs);
     float amax = amax_in ? *amax_in : oracle_nvfp4_amax(x, rows, cols, had, sign_seed);
@@ -493,10 +500,18 @@ int oracle_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int had
             }
             float sbf = (float)oracle_e4m3_decode(sb);
             float inv = 1.0f / (sbf * s_t);
-            for (int i = 0; i < 16; ++i) q[i] = oracle_e2m1_rtn(y[i] * inv);
+            for (int i = 0; i < 16; ++i) {
+                float v = y[i] * inv;
+                if (mode == 2) {
+                    uint64_t idx = (uint64_t)r * (uint64_t)cols + (uint64_t)(b * 16 + i);
+                    q[i] = oracle_e2m1_sr(v, oracle_stream_word(sr_seed, 0, idx));
+                } else {
+                    q[i] = oracle_e2m1_rtn(v);
+                }
+            }
             for (int j = 0; j < 8; ++j) crow[j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
             uint8_t stored = sb;
-            if (renorm) {
+            if (mode == 1) {
                 float num = 0.0f, den = 0.0f;
                 for (int i = 0; i < 16; ++i) {
                     num = fmaf(y[i], y[i], num);

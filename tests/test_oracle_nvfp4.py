@@ -1,13 +1,17 @@
 """Pins of the oracle's NVFP4 quantizer (16-element blocks, E4M3 block scales,
 fp32 tensor scale, renormalization folded into the block scales by
-stochastic rounding).  CPU only.
+stochastic rounding, or stochastic rounding of every element).  CPU only.
 
 The exact renormalization rule is a reading of the Quartet II post (which
 gives the idea and the 0.94..1.06 range but no formula); its bits are
 "parity unpinned" against that paper.  What is pinned here: the rotation and
 tensor amax against scipy, the scale arithmetic by invariants, the
 stochastic rounding of the scales by unbiasedness against an independent
-binary64 computation of the renormalized scale, and the factor's range."""
+binary64 computation of the renormalized scale, and the factor's range; the
+element-SR mode by its neighbours and unbiasedness; and the two properties
+the Quartet II post claims for the renormalized mode: averaged over random
+rotations it is unbiased where round-to-nearest shrinks, and its total error
+is about half that of element SR."""
 import numpy as np
 import pytest
 import scipy.linalg
@@ -55,14 +59,14 @@ def test_amax_and_tensor_scale(tdata, had):
     y = rotated64(tdata, had, 5)
     amax = O.nvfp4_amax(tdata, had, 5)
     assert abs(float(amax) - np.abs(y).max()) <= 1e-6 * np.abs(y).max()
-    _, _, st = O.nvfp4_quantize(tdata, had=had, sign_seed=5, renorm=0)
+    _, _, st = O.nvfp4_quantize(tdata, had=had, sign_seed=5, mode=O.NV_RTN)
     assert st == np.float32(amax) / np.float32(2688.0)          # 6 * 448
-    _, _, st2 = O.nvfp4_quantize(tdata, had=had, sign_seed=5, renorm=0, amax_in=10.0)
+    _, _, st2 = O.nvfp4_quantize(tdata, had=had, sign_seed=5, mode=O.NV_RTN, amax_in=10.0)
     assert st2 == np.float32(10.0) / np.float32(2688.0)
 
 
 def test_block_scale_maps_block_max_near_6(tdata):
-    codes, scales, st = O.nvfp4_quantize(tdata, had=O.HAD_SIGNED, sign_seed=5, renorm=0)
+    codes, scales, st = O.nvfp4_quantize(tdata, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_RTN)
     y = rotated64(tdata, O.HAD_SIGNED, 5)
     sb = np.array([O.e4m3_decode(b) for b in range(256)])[scales]
     mb = np.abs(y).reshape(y.shape[0], -1, 16).max(axis=2)
@@ -78,7 +82,7 @@ def test_block_scale_maps_block_max_near_6(tdata):
 
 def test_renorm_changes_only_scales_and_is_unbiased(tdata):
     x = tdata[:4]
-    c0, s0, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, renorm=0)
+    c0, s0, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_RTN)
     y = rotated64(x, O.HAD_SIGNED, 5)
     sb = np.array([O.e4m3_decode(b) for b in range(256)])[s0]
     # renormalized scale in binary64: s_b * |y|^2 / <y, y_hat>
@@ -89,7 +93,7 @@ def test_renorm_changes_only_scales_and_is_unbiased(tdata):
     acc = np.zeros_like(target)
     acc2 = np.zeros_like(target)
     for seed in range(n):
-        c1, s1, st1 = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, renorm=1, sr_seed=seed)
+        c1, s1, st1 = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_RENORM_SR, sr_seed=seed)
         assert st1 == st and np.array_equal(c1, c0)
         d = np.array([O.e4m3_decode(b) for b in range(256)])[s1]
         acc += d
@@ -107,7 +111,7 @@ def test_renorm_factor_range():
     0.94..1.06 for rotated tensors; check that the bulk lies there."""
     rng = np.random.default_rng(1)
     x = bf16(rng.standard_t(4, (128, 1024)))
-    c0, s0, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=7, renorm=0)
+    c0, s0, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=7, mode=O.NV_RTN)
     y = rotated64(x, O.HAD_SIGNED, 7).reshape(128, -1, 16)
     yhat = dequant(c0, s0, st).reshape(128, -1, 16)
     rho = (y * y).sum(2) / (y * yhat).sum(2)
@@ -121,3 +125,104 @@ def test_zero_tensor_and_bad_args():
     assert st == 1.0 and not c.any() and not s.any()
     with pytest.raises(ValueError):
         O.nvfp4_quantize(np.zeros((2, 24), np.uint16))
+
+
+E4 = np.array([O.e4m3_decode(b) for b in range(256)])
+
+
+def test_element_sr_neighbours_and_scales(tdata):
+    """Element SR keeps mode 0's scales and tensor scale; every code is one
+    of the two E2M1 neighbours of v = y / (s_b s_t) (6 when |v| >= 6)."""
+    x = tdata[:8]
+    c0, s0, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_RTN)
+    c2, s2, st2 = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_ELEMENT_SR, sr_seed=3)
+    assert st2 == st and np.array_equal(s2, s0)
+    assert not np.array_equal(c2, c0)
+    y = rotated64(x, O.HAD_SIGNED, 5)
+    unit = np.repeat(E4[s0] * float(st), 16, axis=1)
+    v = np.abs(y) / unit
+    got = np.abs(dequant(c2, s2, st2)) / unit
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    lo = grid[np.clip(np.searchsorted(grid, v, side="right") - 1, 0, 7)]
+    hi = grid[np.clip(np.searchsorted(grid, v, side="right"), 0, 7)]
+    ok = (np.abs(got - lo) < 1e-9) | (np.abs(got - hi) < 1e-9)
+    assert ok[(v < 6 * (1 - 1e-6)) & (unit > 0)].all()
+    assert (np.abs(got[v >= 6 * (1 + 1e-6)] - 6) < 1e-9).all()
+
+
+def test_element_sr_unbiased(tdata):
+    """Mean over SR seeds of each dequantized element equals y (binary64,
+    independent rotation) where nothing saturates, within 4.5 standard
+    errors of the two-point distribution between the element's grid
+    neighbours (plus one grid step / n, the resolution of a mean of n
+    samples)."""
+    x = tdata[:4, :64]
+    c0, s0, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_RTN)
+    y = rotated64(x, O.HAD_SIGNED, 5)
+    n = 3000
+    acc = np.zeros_like(y)
+    for seed in range(n):
+        c, s, _ = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=5, mode=O.NV_ELEMENT_SR, sr_seed=seed)
+        acc += dequant(c, s, st)
+    mean = acc / n
+    unit = np.repeat(E4[s0] * float(st), 16, axis=1)
+    v = np.abs(y) / unit
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    k = np.clip(np.searchsorted(grid, v, side="right") - 1, 0, 6)
+    step = grid[k + 1] - grid[k]
+    p = np.clip((v - grid[k]) / step, 0, 1)
+    se = step * unit * np.sqrt(p * (1 - p) / n)
+    inside = v < 6 * (1 - 1e-6)
+    assert inside.mean() > 0.9
+    assert (np.abs(mean - y) <= 4.5 * se + step * unit / n + 1e-6 * np.abs(y))[inside].all()
+
+
+def _derotated_mean_coefficient(x, mode, n):
+    """<E[D H^T q(H D x)], x> / <x, x>, the expectation taken over n sign
+    seeds (each with its own SR seed), in binary64."""
+    H = scipy.linalg.hadamard(16) * 0.25
+    xf = f32(x).astype(np.float64)
+    r, c = xf.shape
+    coef = []
+    for seed in range(n):
+        s = O.hadamard_signs(O.HAD_SIGNED, 16, seed).astype(np.float64)
+        cq, sq, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=seed, mode=mode, sr_seed=1000 + seed)
+        back = ((dequant(cq, sq, st).reshape(r, -1, 16) @ H) * s).reshape(r, c)
+        coef.append((back * xf).sum() / (xf * xf).sum())
+    return float(np.mean(coef))
+
+
+def test_renormalized_mode_unbiased_over_rotations():
+    """[QUARTET-II]: quantizing a randomly rotated tensor gives, in
+    expectation, a result collinear with the original, and the per-block
+    renormalization makes it unbiased.  Averaged over 1000 random-sign
+    rotations, round-to-nearest shrinks the tensor by about 0.5 %
+    (coefficient 0.995, standard error 1e-4); the renormalized mode's
+    coefficient is within a third of that distance of 1."""
+    rng = np.random.default_rng(2)
+    x = bf16(rng.standard_t(4, (8, 256)))
+    c_rtn = _derotated_mean_coefficient(x, O.NV_RTN, 1000)
+    c_ren = _derotated_mean_coefficient(x, O.NV_RENORM_SR, 1000)
+    assert c_rtn < 0.997
+    assert abs(1 - c_ren) < 0.35 * abs(1 - c_rtn)
+
+
+def test_total_error_half_of_element_sr():
+    """[QUARTET-II]: with SR only in the FP8 scales the total error comes out
+    about half that of plain (element) SR.  Mean squared error against the
+    rotated tensor over 50 SR seeds on Student-t data: the ratio is 1.99
+    here (accepted: 1.6 .. 2.4).  The post's other figure, a hundredfold
+    smaller error from the scale SR itself, depends on what is compared and
+    is not pinned (measured: the scale SR's own noise is about 1/15 of the
+    element SR error)."""
+    rng = np.random.default_rng(1)
+    x = bf16(rng.standard_t(4, (64, 512)))
+    y = rotated64(x, O.HAD_SIGNED, 7)
+    _, _, st = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=7, mode=O.NV_RTN)
+    me = mr = 0.0
+    for seed in range(50):
+        ce, se, _ = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=7, mode=O.NV_ELEMENT_SR, sr_seed=seed)
+        cr, sr, _ = O.nvfp4_quantize(x, had=O.HAD_SIGNED, sign_seed=7, mode=O.NV_RENORM_SR, sr_seed=seed)
+        me += np.mean((dequant(ce, se, st) - y) ** 2)
+        mr += np.mean((dequant(cr, sr, st) - y) ** 2)
+    assert 1.6 < me / mr < 2.4
