@@ -154,8 +154,9 @@ def nvfp4_bench(args) -> int:
     """The secondary kernel: NVFP4 quantization of the [16384 x 8192]
     Student-t (nu = 4) tensor with the random-sign Hadamard-16 and the renorm
     folded into the E4M3 scales by SR, the tensor amax computed in-library
-    (two passes) and supplied (one pass).  One JSON line; HBM roofline over
-    algorithmic bytes (2.5625 B/element, +2 B/element for the amax pass)."""
+    (two passes) and supplied (one pass); beside it the element-SR mode (one
+    pass).  One JSON line; HBM roofline over algorithmic bytes (2.5625
+    B/element, +2 B/element for the amax pass)."""
     import numpy as np
     import torch
 
@@ -171,7 +172,7 @@ def nvfp4_bench(args) -> int:
     scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
     ts = torch.empty(1, dtype=torch.float32, device=dev)
     ws = torch.empty(F.nvfp4_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
-    F.nvfp4_quantize(x, F.HAD_SIGNED, 7, 1, 11, codes=codes, scales=scales, tensor_scale=ts,
+    F.nvfp4_quantize(x, F.HAD_SIGNED, 7, F.NV_RENORM_SR, 11, codes=codes, scales=scales, tensor_scale=ts,
                      workspace=ws)
     amax = (ts * 2688.0).contiguous()          # the amax the first call found, for the one-pass run
 
@@ -188,12 +189,14 @@ def nvfp4_bench(args) -> int:
         return e0.elapsed_time(e1) / args.steps
 
     el = rows * cols
-    t2 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, 1, 11, codes=codes, scales=scales,
+    t2 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, F.NV_RENORM_SR, 11, codes=codes, scales=scales,
                                         tensor_scale=ts, workspace=ws))
-    t1 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, 1, 11, amax_in=amax, codes=codes,
+    t1 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, F.NV_RENORM_SR, 11, amax_in=amax, codes=codes,
                                         scales=scales, tensor_scale=ts))
+    te = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, F.NV_ELEMENT_SR, 11, amax_in=amax,
+                                        codes=codes, scales=scales, tensor_scale=ts))
     b1, b2 = el * (2 + 0.5 + 1 / 16), el * (2 + 0.5 + 1 / 16 + 2)
-    g2, g1 = b2 / (t2 * 1e-3) / 1e9, b1 / (t1 * 1e-3) / 1e9
+    g2, g1, ge = b2 / (t2 * 1e-3) / 1e9, b1 / (t1 * 1e-3) / 1e9, b1 / (te * 1e-3) / 1e9
     print(json.dumps({
         "metric": "NVFP4 quantize GB/s (16384x8192, SIGNED-16, renorm by SR, amax in-library)",
         "value": g2, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -201,7 +204,8 @@ def nvfp4_bench(args) -> int:
         "config": {"workload": "nvfp4 [16384x8192] Student-t nu=4", "had": "signed-16", "renorm": 1},
         "roofline": {"bound": "hbm", "achieved": g2, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": g2 / HBM_PEAK_GBS, "traffic": None},
-        "one_pass_amax_in": {"ms": t1, "GBps": g1, "frac_hbm": g1 / HBM_PEAK_GBS}}), flush=True)
+        "one_pass_amax_in": {"ms": t1, "GBps": g1, "frac_hbm": g1 / HBM_PEAK_GBS},
+        "element_sr_one_pass": {"ms": te, "GBps": ge, "frac_hbm": ge / HBM_PEAK_GBS}}), flush=True)
     return 0
 
 

@@ -240,7 +240,10 @@ def nvfp4_workspace_bytes(rows: int, cols: int) -> int:
     return int(lib().nvfp4_workspace_bytes(rows, cols))
 
 
-def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, renorm: int = 1,
+NV_RTN, NV_RENORM_SR, NV_ELEMENT_SR = 0, 1, 2   # nvfp4_mode
+
+
+def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, mode: int = NV_RENORM_SR,
                    sr_seed: int = 0, amax_in: torch.Tensor | None = None,
                    codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
                    tensor_scale: torch.Tensor | None = None,
@@ -255,7 +258,7 @@ def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, r
     tensor_scale = torch.empty(1, dtype=torch.float32, device=dev) if tensor_scale is None else tensor_scale
     if amax_in is None and workspace is None:
         workspace = torch.empty(nvfp4_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
-    _check(lib().nvfp4_quantize(x.data_ptr(), rows, cols, had, sign_seed & (2 ** 64 - 1), renorm,
+    _check(lib().nvfp4_quantize(x.data_ptr(), rows, cols, had, sign_seed & (2 ** 64 - 1), mode,
                                 sr_seed & (2 ** 64 - 1), _ptr(amax_in), codes.data_ptr(),
                                 scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),
                                 0 if workspace is None else workspace.numel() * workspace.element_size(),

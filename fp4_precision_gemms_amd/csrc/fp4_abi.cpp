@@ -144,11 +144,11 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols) {
 }
 
 fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
-                          uint64_t sign_seed, int renorm, uint64_t sr_seed, const float* amax_in,
+                          uint64_t sign_seed, nvfp4_mode mode, uint64_t sr_seed, const float* amax_in,
                           uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale,
                           void* workspace, size_t workspace_bytes, void* stream) {
     if (had != FP4_HAD_NONE && had != FP4_HAD_DET && had != FP4_HAD_SIGNED) return FP4_ERR_ENUM;
-    if (renorm != 0 && renorm != 1) return FP4_ERR_ENUM;
+    if (mode != NVFP4_RTN && mode != NVFP4_RENORM_SR && mode != NVFP4_ELEMENT_SR) return FP4_ERR_ENUM;
     if (!x_bf16 || !codes || !scales_e4m3 || !tensor_scale) return FP4_ERR_NULL;
     if (rows <= 0 || cols <= 0 || cols % 16 || !product_ok(rows, cols)) return FP4_ERR_SHAPE;
     if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales_e4m3) ||
@@ -159,7 +159,7 @@ fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_ha
             return FP4_ERR_WORKSPACE;
         if (!aligned16(workspace)) return FP4_ERR_ALIGN;
     }
-    return from_hip(fp4dev::launch_nvfp4(x_bf16, rows, cols, (int)had, sign_seed, renorm, sr_seed,
+    return from_hip(fp4dev::launch_nvfp4(x_bf16, rows, cols, (int)had, sign_seed, (int)mode, sr_seed,
                                          amax_in, codes, scales_e4m3, tensor_scale, workspace,
                                          (hipStream_t)stream));
 }

@@ -34,10 +34,11 @@ hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* b
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* c,
                           int out_bf16, int accumulate, hipStream_t st);
 
-// NVFP4 quantization; amax_dev is either the caller's amax_in or the
-// workspace the amax pass writes.
+// NVFP4 quantization (mode: 0 RTN, 1 renormalized scales by SR, 2 element
+// SR); amax_dev is either the caller's amax_in or the workspace the amax pass
+// writes.
 hipError_t launch_nvfp4(const void* x, int64_t rows, int64_t cols, int had, uint64_t sign_seed,
-                        int renorm, uint64_t sr_seed, const float* amax_in, uint8_t* codes,
+                        int mode, uint64_t sr_seed, const float* amax_in, uint8_t* codes,
                         uint8_t* scales, float* tensor_scale, void* workspace, hipStream_t st);
 
 uint32_t host_sign_word(int had, uint64_t seed);

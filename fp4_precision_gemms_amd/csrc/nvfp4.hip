@@ -1,13 +1,14 @@
 // nvfp4.hip -- NVFP4 quantization (16-element blocks, E4M3 block scales, fp32
 // tensor scale) with the renormalization folded into the block scales by
-// stochastic rounding.
+// stochastic rounding, or with every element rounded stochastically.
 //
 // [QUARTET-II] "Quartet II -- обучение в NVFP4 с точными несмещёнными
 // градиентами": NVFP4 carries FP8 block scales; a randomly rotated tensor,
 // once quantized, is collinear with the original in expectation and a
 // renormalization makes it unbiased; the factor is too fine for FP8 scales,
 // so it is put into the scales by stochastic rounding -- the scales only,
-// not every FP4 element.  [NV-NVFP4] "NVIDIA создала метод обучения
+// not every FP4 element as in the recipe it compares against (kept here as
+// the element-SR mode).  [NV-NVFP4] "NVIDIA создала метод обучения
 // нейросетей в 4-bit точности", section "Как это работает": 16x16 random
 // Hadamard transforms on gradient inputs.
 //
@@ -20,7 +21,10 @@
 //               stochastically toward |y|^2 / (s_t sum y_i q_i).  The codes
 //               come from the hardware FP4 conversion of fl(y_i * inv) with
 //               scale 1 (round to nearest even, saturating -- the rule the
-//               MX quantizers check bit-exact), q_i from its inverse.
+//               MX quantizers check bit-exact), q_i from its inverse; in the
+//               element-SR mode from the MX quantizers' stochastic rounding
+//               with the element stream (purpose 0, index = row-major
+//               position: two Philox calls per 8-element chunk).
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
@@ -135,12 +139,14 @@ __device__ __forceinline__ void decode8(uint32_t w, float* out) {
     r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); out[6] = r.x; out[7] = r.y;
 }
 
-template <bool HAD, bool RENORM>
+// MODE 0: RTN; 1: RTN + renormalized scale by SR; 2: element SR.
+template <bool HAD, int MODE>
 __global__ __launch_bounds__(kThreads) void nv_quant(
     const uint4* __restrict__ x, int64_t nchunks, uint32_t sign_word, const float* __restrict__ amax_p,
     uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tensor_scale) {
     const float amax = *amax_p;
+    constexpr bool RENORM = MODE == 1;
     const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;   // 6 * 448
     const float six_st = 6.0f * s_t;
     if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
@@ -180,7 +186,16 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
             float v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[t] = y[t] * inv;
-            word = encode8_unit(v);
+            if constexpr (MODE == 2) {
+                // elements 8g .. 8g+7: words of stream counters 2g and 2g + 1
+                const uint4 r0 = stream4(sr_seed, 0u, (uint64_t)(2 * g));
+                const uint4 r1 = stream4(sr_seed, 0u, (uint64_t)(2 * g + 1));
+                const uint32_t uw[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) word |= e2m1_sr(v[t], uw[t]) << (4 * t);
+            } else {
+                word = encode8_unit(v);
+            }
             if constexpr (RENORM) {
                 // sequential binary32 fmaf chains over the 16 elements in order:
                 // the lower lane's partial sums seed the upper lane's chain
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
 }
 
 template <bool HAD>
-hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw, int renorm,
+hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw, int mode,
                          uint64_t sr_seed, const float* amax_in, uint8_t* codes, uint8_t* scales,
                          float* tensor_scale, void* workspace, hipStream_t st) {
     const int64_t nchunks = rows * cols / 8;
@@ -229,12 +244,16 @@ hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw,
         amax_p = (const float*)ws;
     }
     const int64_t qblocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
-    if (renorm) {
-        hipLaunchKernelGGL((nv_quant<HAD, true>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
+    if (mode == 1) {
+        hipLaunchKernelGGL((nv_quant<HAD, 1>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
+                           (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
+                           tensor_scale);
+    } else if (mode == 2) {
+        hipLaunchKernelGGL((nv_quant<HAD, 2>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
                            (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
                            tensor_scale);
     } else {
-        hipLaunchKernelGGL((nv_quant<HAD, false>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((nv_quant<HAD, 0>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
                            (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
                            tensor_scale);
     }
@@ -244,12 +263,12 @@ hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw,
 }  // namespace
 
 hipError_t launch_nvfp4(const void* x, int64_t rows, int64_t cols, int had, uint64_t sign_seed,
-                        int renorm, uint64_t sr_seed, const float* amax_in, uint8_t* codes,
+                        int mode, uint64_t sr_seed, const float* amax_in, uint8_t* codes,
                         uint8_t* scales, float* tensor_scale, void* workspace, hipStream_t st) {
     if (had == 0)
-        return launch_nv_had<false>(x, rows, cols, 0u, renorm, sr_seed, amax_in, codes, scales,
+        return launch_nv_had<false>(x, rows, cols, 0u, mode, sr_seed, amax_in, codes, scales,
                                     tensor_scale, workspace, st);
-    return launch_nv_had<true>(x, rows, cols, host_sign_word(had, sign_seed), renorm, sr_seed,
+    return launch_nv_had<true>(x, rows, cols, host_sign_word(had, sign_seed), mode, sr_seed,
                                amax_in, codes, scales, tensor_scale, workspace, st);
 }
 

@@ -9,7 +9,7 @@
  * plain (the same every step) or after seeded random sign flips.  A second
  * quantizer produces NVFP4 (16-element blocks, E4M3 block scales, an fp32
  * tensor scale) with a renormalization folded into the block scales by
- * stochastic rounding.
+ * stochastic rounding, or with stochastic rounding of every element.
  *
  * Pages this interface follows (title, then section):
  *   [AMD-MXFP4]  "Pretraining large language models with MXFP4 on Native FP4
@@ -226,12 +226,25 @@ fp4_status fp4_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, 
                        int64_t M, int64_t N, int64_t Kc, void* c, fp4_out_dtype out,
                        int accumulate, void* stream);
 
+/* Rounding of nvfp4_quantize.  [QUARTET-II] contrasts two ways to make the
+ * quantized gradient unbiased: stochastic rounding of every FP4 element
+ * (NVIDIA's recipe, also [NV-NVFP4, "Как это работает"]) and elements
+ * rounded to nearest with a per-block renormalization put into the FP8
+ * scales by stochastic rounding (Quartet II). */
+typedef enum {
+    NVFP4_RTN = 0,         /* elements to nearest, scales to nearest        */
+    NVFP4_RENORM_SR = 1,   /* elements to nearest, renormalized scale by SR */
+    NVFP4_ELEMENT_SR = 2   /* elements by SR, scales to nearest             */
+} nvfp4_mode;
+
 /*
  * nvfp4_quantize -- NVFP4 quantization of bf16 x[rows, cols] along cols in
  * 16-element blocks.  [QUARTET-II]: FP4 elements with FP8 (E4M3) block
  * scales; the renormalization factor of a rotated tensor is folded into the
  * FP8 scales by stochastic rounding, the elements themselves are rounded to
- * nearest.  [NV-NVFP4, "Как это работает"]: 16x16 random Hadamard transforms.
+ * nearest (mode NVFP4_RENORM_SR); the alternative it compares against rounds
+ * every element stochastically (NVFP4_ELEMENT_SR).  [NV-NVFP4, "Как это
+ * работает"]: 16x16 random Hadamard transforms.
  *   1. y = 16-block transform of each row (had as in fp4_hadamard_quantize
  *      with had_n = 16; NONE, DET or SIGNED).
  *   2. A = max |y| over the tensor, or *amax_in (a device float) when
@@ -239,8 +252,13 @@ fp4_status fp4_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, 
  *      *tensor_scale = s_t (a device float).
  *   3. per block: s_b = E4M3_RNE(fl(m_b / fl(6 s_t))) saturating at 448;
  *      s_b = 0 gives all-zero codes and scale 0.  Otherwise
- *      v_i = y_i * fl(1 / fl(s_b s_t)), codes = E2M1 RTN of v_i.
- *   4. renorm = 1: num = sum y_i^2, den = sum y_i e2m1(code_i) as binary32
+ *      v_i = y_i * fl(1 / fl(s_b s_t)), codes = E2M1 RTN of v_i; with
+ *      NVFP4_ELEMENT_SR codes = E2M1 SR of v_i (the rule of
+ *      fp4_hadamard_quantize: |v| >= 6 gives 6, else up iff
+ *      (u >> 8) 2^-24 < p) with u = word (idx & 3) of
+ *      Philox4x32-10(key = sr_seed, counter = (idx >> 2 as (lo, hi), 0, 0)),
+ *      idx = r * cols + c, and the stored scale is s_b.
+ *   4. NVFP4_RENORM_SR: num = sum y_i^2, den = sum y_i e2m1(code_i) as binary32
  *      fmaf chains in element order; if den > 0 the stored scale is
  *      E4M3_SR(fl(num / fl(s_t den))) with u = word (blk & 3) of
  *      Philox4x32-10(key = sr_seed, counter = (blk >> 2 as (lo, hi), 2, 0)),
@@ -254,7 +272,7 @@ fp4_status fp4_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, 
  * amax_in 4-byte aligned).
  */
 fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
-                          uint64_t sign_seed, int renorm, uint64_t sr_seed,
+                          uint64_t sign_seed, nvfp4_mode mode, uint64_t sr_seed,
                           const float* amax_in, uint8_t* codes, uint8_t* scales_e4m3,
                           float* tensor_scale, void* workspace, size_t workspace_bytes,
                           void* stream);

@@ -158,13 +158,14 @@ def test_gemm_mx_errors(L):
 
 
 def test_nvfp4_errors(L):
-    def call(x=A, rows=32, cols=64, had=2, renorm=1, amax=None, codes=A, scales=A, ts=A,
+    def call(x=A, rows=32, cols=64, had=2, mode=1, amax=None, codes=A, scales=A, ts=A,
              ws=A, wsb=256):
-        return L.nvfp4_quantize(x, rows, cols, had, 0, renorm, 0, amax, codes, scales, ts, ws, wsb,
+        return L.nvfp4_quantize(x, rows, cols, had, 0, mode, 0, amax, codes, scales, ts, ws, wsb,
                                 None)
 
     assert call(had=5) == ERR_ENUM
-    assert call(renorm=2) == ERR_ENUM
+    assert call(mode=3) == ERR_ENUM
+    assert call(mode=-1) == ERR_ENUM
     assert call(x=None) == ERR_NULL
     assert call(ts=None) == ERR_NULL
     assert call(cols=24) == ERR_SHAPE

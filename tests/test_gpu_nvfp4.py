@@ -1,6 +1,7 @@
 """GPU parity of nvfp4_quantize against the oracle: codes, E4M3 scales and
 the tensor scale bit-exact, with the amax computed in the library (two
-passes) or supplied (one pass), renormalization on and off."""
+passes) or supplied (one pass), in each rounding mode (elements to nearest
+with or without the renormalized scale, or every element stochastic)."""
 import numpy as np
 import pytest
 import torch
@@ -15,36 +16,36 @@ pytestmark = pytest.mark.gpu
 HD = {O.HAD_NONE: F.HAD_NONE, O.HAD_DET: F.HAD_DET, O.HAD_SIGNED: F.HAD_SIGNED}
 
 
-def gpu_nv(bits, had, seed, renorm, sr_seed, amax_in=None):
+def gpu_nv(bits, had, seed, mode, sr_seed, amax_in=None):
     need_gpu()
     x = to_gpu_bf16(bits)
     rows, cols = bits.shape
     codes, scales = sentinel_u8((rows, cols // 2)), sentinel_u8((rows, cols // 16))
     ts = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
     a = None if amax_in is None else torch.tensor([amax_in], dtype=torch.float32, device="cuda")
-    F.nvfp4_quantize(x, HD[had], seed, renorm, sr_seed, amax_in=a, codes=codes, scales=scales,
+    F.nvfp4_quantize(x, HD[had], seed, mode, sr_seed, amax_in=a, codes=codes, scales=scales,
                      tensor_scale=ts)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy(), np.float32(ts.item())
 
 
-def check(bits, had, seed, renorm, sr_seed, amax_in=None, what=""):
-    say("nvfp4", what, bits.shape, had, renorm, amax_in)
-    gc, gs, gt = gpu_nv(bits, had, seed, renorm, sr_seed, amax_in)
-    rc, rs, rt = O.nvfp4_quantize(bits, had, seed, renorm, sr_seed, amax_in)
+def check(bits, had, seed, mode, sr_seed, amax_in=None, what=""):
+    say("nvfp4", what, bits.shape, had, mode, amax_in)
+    gc, gs, gt = gpu_nv(bits, had, seed, mode, sr_seed, amax_in)
+    rc, rs, rt = O.nvfp4_quantize(bits, had, seed, mode, sr_seed, amax_in)
     assert gt.view(np.uint32) == rt.view(np.uint32), (gt, rt)
     assert np.array_equal(gs, rs), ("scales", (gs != rs).sum(), np.argwhere(gs != rs)[:5].tolist())
     assert np.array_equal(gc, rc), ("codes", (gc != rc).sum(), np.argwhere(gc != rc)[:5].tolist())
 
 
 @pytest.mark.parametrize("had", [O.HAD_NONE, O.HAD_DET, O.HAD_SIGNED])
-@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("mode", [O.NV_RTN, O.NV_RENORM_SR, O.NV_ELEMENT_SR])
 @pytest.mark.parametrize("shape", [(64, 256), (3, 16), (130, 1040)])
-def test_nvfp4_parity(had, renorm, shape):
+def test_nvfp4_parity(had, mode, shape):
     rng = np.random.default_rng(shape[0] + shape[1])
     bits = bf16_bits(rng.standard_t(4, shape))
-    check(bits, had, 9, renorm, 4, what="t4")
-    check(bits, had, 9, renorm, 4, amax_in=3.5, what="amax_in")
+    check(bits, had, 9, mode, 4, what="t4")
+    check(bits, had, 9, mode, 4, amax_in=3.5, what="amax_in")
 
 
 def test_nvfp4_edge_values():
@@ -57,6 +58,7 @@ def test_nvfp4_edge_values():
     check(bf16_bits(v), O.HAD_SIGNED, 1, 1, 2, what="edge")
     check(bf16_bits(v), O.HAD_NONE, 1, 1, 2, what="edge")
     check(bf16_bits(np.zeros((4, 32))), O.HAD_SIGNED, 1, 1, 2, what="zeros")
+    check(bf16_bits(v), O.HAD_SIGNED, 1, O.NV_ELEMENT_SR, 2, what="edge element SR")
 
 
 @pytest.mark.slow
@@ -64,4 +66,5 @@ def test_nvfp4_full_size():
     """The [16384 x 8192] Student-t (nu = 4) tensor, whole, as benchmarked."""
     w = W.WORKLOADS["nvfp4"]
     bits = W.tensor(w, "x")
-    check(bits, O.HAD_SIGNED, 123, 1, 77, what="full")
+    check(bits, O.HAD_SIGNED, 123, O.NV_RENORM_SR, 77, what="full")
+    check(bits, O.HAD_SIGNED, 123, O.NV_ELEMENT_SR, 77, what="full element SR")
