@@ -12,6 +12,7 @@ are synthetic bf16 tensors resident in HBM before timing starts.
                     [--copy-calibration]
     python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
     python bench.py --nvfp4                            (the secondary NVFP4 quantizer)
+    python bench.py --layer                            (the whole linear layer: three GEMMs)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
 (2 T N K flops over the whole step); the roofline object describes the
@@ -209,6 +210,95 @@ def nvfp4_bench(args) -> int:
     return 0
 
 
+def layer_bench(args) -> int:
+    """The whole MXFP4 linear layer on the gate/up shape: X[T, K], W[N, K]
+    and dY[T, N] each quantized once per direction by the dual quantizer
+    (rows: along the first axis, Hadamard-32 on the Wgrad operands X and dY;
+    cols: along the second axis, no rotation), then Fprop Y = X W^T, Dgrad
+    dX = dY W and Wgrad dW = dY^T X through the role entry points (fp32
+    outputs).  One JSON line: 3 * 2 T N K flops over the step, and each
+    launch's average time from HIP events around it."""
+    import numpy as np
+    import torch
+
+    import fp4_precision_gemms_amd as F
+    import workloads as W
+
+    w = W.WORKLOADS["gate_up"]
+    T, N, K = w.T, w.N, w.K
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    X, Wt, dY = up(W.tensor(w, "X")), up(W.tensor(w, "W")), up(W.tensor(w, "dY"))
+
+    def bufs(rows, cols):
+        shapes = F.mx_shapes(rows, cols, F.AXIS_ROWS) + F.mx_shapes(rows, cols, F.AXIS_COLS)
+        return [torch.empty(sh, dtype=torch.uint8, device=dev) for sh in shapes]
+
+    qx, qw, qdy = bufs(T, K), bufs(N, K), bufs(T, N)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dx = torch.empty((T, K), dtype=torch.float32, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    launches = [
+        ("quant_X_dual", lambda: F.fp4_hadamard_quantize_dual(X, 32, F.HAD_DET, out=qx)),
+        ("quant_W_dual", lambda: F.fp4_hadamard_quantize_dual(Wt, 32, F.HAD_NONE, out=qw)),
+        ("quant_dY_dual", lambda: F.fp4_hadamard_quantize_dual(dY, 32, F.HAD_DET, out=qdy)),
+        ("fprop", lambda: F.fp4_gemm_fprop(qx[2], qx[3], qw[2], qw[3], out=y)),
+        ("dgrad", lambda: F.fp4_gemm_dgrad(qdy[2], qdy[3], qw[0], qw[1], out=dx)),
+        ("wgrad", lambda: F.fp4_gemm_wgrad(qdy[0], qdy[1], qx[0], qx[1], out=dw)),
+    ]
+
+    def step():
+        for _, fn in launches:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / args.steps
+    # per-launch times, in a second timed pass with events around each launch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.steps)]
+    for i in range(args.steps):
+        for (a, b), (_, fn) in zip(ev[i], launches):
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize(dev)
+    per = {name: 1e3 * sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)) / args.steps
+           for j, (name, _) in enumerate(launches)}
+    flop = 2.0 * T * N * K
+    qbytes = {"quant_X_dual": T * K * (2 + 1 + 1 / 16), "quant_W_dual": N * K * (2 + 1 + 1 / 16),
+              "quant_dY_dual": T * N * (2 + 1 + 1 / 16)}
+    breakdown = {}
+    for name, us in per.items():
+        breakdown[name + "_us"] = us
+        if name in qbytes:
+            breakdown[name + "_GBps"] = qbytes[name] / (us * 1e-6) / 1e9
+        else:
+            breakdown[name + "_TFLOPs"] = flop / (us * 1e-6) / 1e12
+    gemm_us = min(per["fprop"], per["dgrad"], per["wgrad"])
+    print(json.dumps({
+        "metric": "MXFP4 linear layer TFLOP/s (Fprop + Dgrad + Wgrad incl. dual quantization, 8192x14336x4096)",
+        "value": 3 * flop / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "gate_up linear layer, all three GEMMs", "T": T, "N": N, "K": K,
+                   "hadamard": "deterministic-32 on the Wgrad operands", "rounding": "rtn",
+                   "outputs": "fp32"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_mx_tn (fastest of the three roles)",
+                     "achieved": flop / (gemm_us * 1e-6) / 1e12, "peak": MXFP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flop / (gemm_us * 1e-6) / 1e12 / MXFP4_PEAK_TFLOPS,
+                     "traffic": None},
+        "breakdown": breakdown}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +313,7 @@ def main() -> int:
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 counter runs and exit")
     ap.add_argument("--nvfp4", action="store_true", help="time the NVFP4 quantizer instead")
+    ap.add_argument("--layer", action="store_true", help="time the whole linear layer instead")
     args = ap.parse_args()
     if args.counters:
         return counter_summary(*args.counters)
@@ -233,6 +324,8 @@ def main() -> int:
 
     if args.nvfp4:
         return nvfp4_bench(args)
+    if args.layer:
+        return layer_bench(args)
 
     import numpy as np
     import torch

@@ -131,15 +131,21 @@ def fp4_hadamard_quantize(x: torch.Tensor, axis: int = AXIS_COLS, had_n: int = 3
 def fp4_hadamard_quantize_dual(x: torch.Tensor, had_n_rows: int = 32, had_rows: int = HAD_NONE,
                                sign_seed_rows: int = 0, rnd_rows: int = RTN, sr_seed_rows: int = 0,
                                had_n_cols: int = 32, had_cols: int = HAD_NONE, sign_seed_cols: int = 0,
-                               rnd_cols: int = RTN, sr_seed_cols: int = 0, stream=None):
+                               rnd_cols: int = RTN, sr_seed_cols: int = 0, out=None, stream=None):
     """Both quantizations of bf16 x[rows, cols] from one read: (codes, scales)
     along rows (as AXIS_ROWS) and along cols (as AXIS_COLS), each with its own
-    rotation and rounding (see include/fp4.h)."""
+    rotation and rounding (see include/fp4.h).  `out`: optional preallocated
+    (codes_rows, scales_rows, codes_cols, scales_cols)."""
     _need(x, torch.bfloat16, "x")
     rows, cols = x.shape
     (cr, sr), (cc, sc) = mx_shapes(rows, cols, AXIS_ROWS), mx_shapes(rows, cols, AXIS_COLS)
     dev = x.device
-    out = [torch.empty(sh, dtype=torch.uint8, device=dev) for sh in (cr, sr, cc, sc)]
+    if out is None:
+        out = [torch.empty(sh, dtype=torch.uint8, device=dev) for sh in (cr, sr, cc, sc)]
+    for t, sh in zip(out, (cr, sr, cc, sc)):
+        _need(t, torch.uint8, "output")
+        if tuple(t.shape) != tuple(sh):
+            raise ValueError("output of shape %s expected, got %s" % (sh, tuple(t.shape)))
     m = 2 ** 64 - 1
     _check(lib().fp4_hadamard_quantize_dual(
         x.data_ptr(), rows, cols, had_n_rows, had_rows, sign_seed_rows & m, rnd_rows, sr_seed_rows & m,
