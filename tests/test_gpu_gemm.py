@@ -154,3 +154,24 @@ def test_gemm_tile_shapes_sampled(M, N, K):
     ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
     gemm_check(got[mi, ni], ref, mag, TOL)
     assert np.isfinite(got).all()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("K", [2 ** 24 - 256, 2 ** 24 - 32])
+def test_gemm_largest_contraction(K):
+    """The largest contraction the ABI accepts (K < 2^24), with and without a
+    partial last stage, and M = 256 rows: the A operand is just under 2^31
+    bytes, so the kernel's 32-bit buffer offsets reach their limit.  64
+    entries (corners, tile edges, random) recomputed by the oracle."""
+    M, N = 256, 40
+    rng = np.random.default_rng(K)
+    aq, as_ = rand_operands(rng, M, K)
+    bq, bs = rand_operands(rng, N, K)
+    assert aq.nbytes < 2 ** 31 and aq.nbytes > 2 ** 31 - 2 ** 24
+    say("gemm largest contraction", M, N, K)
+    got = run(F.fp4_gemm_fprop, (aq, as_, bq, bs), (M, N))
+    mi = np.concatenate([[0, 0, M - 1, M - 1, 223, 224], rng.integers(0, M, 58)])
+    ni = np.concatenate([[0, N - 1, 0, N - 1, 5, 39], rng.integers(0, N, 58)])
+    ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
+    gemm_check(got[mi, ni], ref, mag, TOL)
+    assert np.isfinite(got).all()

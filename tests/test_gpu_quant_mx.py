@@ -172,3 +172,34 @@ def test_quant_parity_full_size_sampled_rows(wname, tname, axis, had, rnd):
     for r0 in (0, R // 2 - 32, R - 64):
         rc, rs = O.quant_mx(bits, axis, 32, had, 2024, rnd, 11, r0=r0, r1=r0 + 64)
         assert_same((gc[r0:r0 + 64], gs[r0:r0 + 64]), (rc, rs), "%s %s rows %d" % (wname, tname, r0))
+
+
+@pytest.mark.slow
+def test_quant_input_over_2gib():
+    """An input of 2^31 bytes or more: x[33024, 32768] bf16 (2.16 GB).  The
+    transposed quantizer takes its 64-bit-indexed kernel and the dual entry
+    point its two-launch fallback; three ranges of 32 logical rows of every
+    output are recomputed by the oracle."""
+    need_gpu()
+    rows, cols = 33024, 32768
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((rows, cols), generator=g, device="cuda").to(torch.bfloat16)
+    bits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert bits.nbytes >= 2 ** 31
+    say("quant over 2 GiB", rows, cols)
+    codes, scales = F.fp4_hadamard_quantize(x, F.AXIS_ROWS, 32, F.HAD_DET, 0, F.RTN, 0)
+    rq, rs, cq, cs = F.fp4_hadamard_quantize_dual(x, 32, F.HAD_SIGNED, 9, F.RTN, 0, 32, F.HAD_NONE)
+    torch.cuda.synchronize()
+    got = {
+        "rows": (codes.cpu().numpy(), ungroup_scales(scales.cpu().numpy(), rows // 32),
+                 (O.AXIS_ROWS, O.HAD_DET, 0)),
+        "dual rows": (rq.cpu().numpy(), ungroup_scales(rs.cpu().numpy(), rows // 32),
+                      (O.AXIS_ROWS, O.HAD_SIGNED, 9)),
+        "dual cols": (cq.cpu().numpy(), ungroup_scales(cs.cpu().numpy(), cols // 32),
+                      (O.AXIS_COLS, O.HAD_NONE, 0)),
+    }
+    for what, (gc, gs, (axis, had, seed)) in got.items():
+        R = gc.shape[0]
+        for r0 in (0, R // 2 - 16, R - 32):
+            rc, rsc = O.quant_mx(bits, axis, 32, had, seed, O.RND_RTN, 0, r0=r0, r1=r0 + 32)
+            assert_same((gc[r0:r0 + 32], gs[r0:r0 + 32]), (rc, rsc), "%s rows %d" % (what, r0))
