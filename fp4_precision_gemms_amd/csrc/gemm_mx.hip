@@ -44,6 +44,11 @@
 //     the block index is remapped so that each XCD works on a contiguous run
 //     of tiles, ordered in groups of GM tile-rows, so tiles that share A and
 //     B rows meet in the same L2.
+//   - Persistent workgroups (one per CU) loop over their tiles.  The output
+//     leaves through LDS in whole rows per store instruction; when a tile and
+//     the workgroup's next tile are both full, the next tile's first stage is
+//     issued before the epilogue (into stage buffer 0, the epilogue staging
+//     in buffer 1), so its latency hides behind the stores.
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
