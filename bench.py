@@ -15,9 +15,11 @@ are synthetic bf16 tensors resident in HBM before timing starts.
     python bench.py --layer                            (the whole linear layer: three GEMMs)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
-(2 T N K flops over the whole step); the roofline object describes the
-dominant kernel (the GEMM) from per-launch HIP events; cpu_baseline times
-the plain CPU oracle on a bounded sample of the same workload.
+(2 T N K flops over the whole step, the K timed steps holding nothing but
+their launches); the roofline object describes the dominant kernel (the
+GEMM) from HIP events around each launch over a second pass of K steps;
+cpu_baseline times the plain CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -368,15 +370,22 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
+    # the timed steps: nothing but the two launches per step (an event record
+    # between launches costs about 3 % of the step)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        step(events[i])
+        step()
     stop.record(stream)
     torch.cuda.synchronize(dev)
     ms_step = start.elapsed_time(stop) / args.steps
+    # per-launch durations: the same number of steps again, HIP events on the
+    # launch stream around each launch
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize(dev)
 
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
