@@ -13,13 +13,17 @@ are synthetic bf16 tensors resident in HBM before timing starts.
     python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
     python bench.py --nvfp4                            (the secondary NVFP4 quantizer)
     python bench.py --layer                            (the whole linear layer: three GEMMs)
+    python bench.py --mfma-ceiling                     (only the MFMA-rate measurement aid)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
 (2 T N K flops over the whole step, the K timed steps holding nothing but
 their launches); the roofline object describes the dominant kernel (the
 GEMM) from HIP events around each launch over a second pass of K steps;
 cpu_baseline times the plain CPU oracle on a bounded sample of the same
-workload.
+workload; mfma_ceiling is the scaled FP4 MFMA rate the card sustains on
+random operands with no memory traffic at all (libfp4calib.so), measured
+after the timed steps, and the shader clock it ran at -- the bound the
+card's power limit puts on any GEMM on such data.
 """
 from __future__ import annotations
 
@@ -316,6 +320,10 @@ def main() -> int:
                     help="summarize two rocprofv3 counter runs and exit")
     ap.add_argument("--nvfp4", action="store_true", help="time the NVFP4 quantizer instead")
     ap.add_argument("--layer", action="store_true", help="time the whole linear layer instead")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the MFMA-only rate on random operands (libfp4calib.so)")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="leave the MFMA-only measurement out of the default run")
     args = ap.parse_args()
     if args.counters:
         return counter_summary(*args.counters)
@@ -328,6 +336,12 @@ def main() -> int:
         return nvfp4_bench(args)
     if args.layer:
         return layer_bench(args)
+    if args.mfma_ceiling:
+        import torch
+        from fp4_precision_gemms_amd import calib
+        print(json.dumps({"mfma_ceiling": calib.mfma_ceiling(torch.device("cuda:0")),
+                          "peak_TFLOPs": MXFP4_PEAK_TFLOPS}), flush=True)
+        return 0
 
     import numpy as np
     import torch
@@ -418,6 +432,12 @@ def main() -> int:
                       "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
                       "gemm_TFLOPs": gemm_tflops},
     }
+    if not args.no_mfma_ceiling:
+        from fp4_precision_gemms_amd import calib
+        ceil = calib.mfma_ceiling(dev)
+        ceil["frac_of_peak"] = ceil["value"] / MXFP4_PEAK_TFLOPS
+        ceil["gemm_frac_of_ceiling"] = gemm_tflops / ceil["value"]
+        out["mfma_ceiling"] = ceil
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
-"""Builds libfp4.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Builds libfp4.so (the HIP kernels and the C ABI) in-tree for gfx950, and
+beside it libfp4calib.so, the MFMA-rate measurement aid (include/fp4_calib.h).
 
     python -m fp4_precision_gemms_amd.build
 
@@ -21,8 +22,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libfp4.so")
+CALIB_LIB_PATH = os.path.join(HERE, "libfp4calib.so")
 
 SOURCES = ["fp4_abi.cpp", "quant_mx.hip", "gemm_mx.hip", "nvfp4.hip"]
+CALIB_SOURCES = ["calib_mfma.hip"]
 ARCH = "gfx950"
 
 
@@ -48,19 +51,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libfp4.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _link(objs: list[str], path: str) -> None:
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libfp4.so and libfp4calib.so; returns
+    the path of libfp4.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB_PATH)
     if verbose:
-        print("built", LIB_PATH)
+        print("built", LIB_PATH, "and", CALIB_LIB_PATH)
     return LIB_PATH
 
 

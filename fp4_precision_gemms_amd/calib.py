@@ -1,0 +1,71 @@
+"""Binding of libfp4calib.so (include/fp4_calib.h): the scaled FP4 MFMA rate
+the card sustains on random operands under its power limit, with the shader
+clock it ran at.  A measurement aid for the GEMM's roofline, not part of the
+quantized-GEMM path."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4calib.so")
+REFCLK_HZ = 100e6          # the reference clock behind s_memrealtime
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfp4calib.so is not built: run `python -m fp4_precision_gemms_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fp4_calib_mfma_src_bytes.argtypes = [ctypes.c_int]
+        L.fp4_calib_mfma_src_bytes.restype = ctypes.c_size_t
+        L.fp4_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.fp4_calib_mfma_flops.restype = ctypes.c_double
+        L.fp4_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.fp4_calib_mfma.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def mfma_ceiling(device, iters: int = 20000, warmup: int = 20, launches: int = 10, seed: int = 0) -> dict:
+    """Runs the MFMA-only loop on one workgroup per CU: `warmup` launches to
+    let the clocks settle, then `launches` timed ones (HIP events on the
+    launch stream).  Returns TFLOP/s and the median shader clock over all
+    waves of the timed launches."""
+    L = lib()
+    grid = torch.cuda.get_device_properties(device).multi_processor_count
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    src = torch.randint(0, 256, (L.fp4_calib_mfma_src_bytes(grid),), dtype=torch.uint8, device=device,
+                        generator=g)
+    out = torch.empty(grid * 256, dtype=torch.float32, device=device)
+    clocks = torch.zeros((launches, grid * 4, 2), dtype=torch.int64, device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def launch(ck):
+        st = L.fp4_calib_mfma(src.data_ptr(), grid, iters, out.data_ptr(), ck.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("fp4_calib_mfma failed with status %d" % st)
+
+    for _ in range(warmup):
+        launch(clocks[0])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(launches):
+        launch(clocks[i])
+    e1.record(stream)
+    torch.cuda.synchronize(device)
+    sec = e0.elapsed_time(e1) * 1e-3 / launches
+    ck = clocks.double().cpu()
+    sclk = (ck[..., 0] / ck[..., 1]).median().item() * REFCLK_HZ
+    tflops = L.fp4_calib_mfma_flops(grid, iters) / sec / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "sclk_GHz": sclk / 1e9, "grid": grid, "iters": iters,
+            "ms_per_launch": sec * 1e3,
+            "what": "scaled FP4 MFMA 32x32x64 only, random E2M1 operands in registers, the Wgrad "
+                    "GEMM's wave tile (7x2 accumulators, two fragment sets), one workgroup of 4 "
+                    "waves per CU"}

@@ -1,0 +1,54 @@
+"""libfp4calib.so without a GPU: it loads, exports what include/fp4_calib.h
+declares, counts its work as documented, and rejects bad arguments before
+any HIP call (the fake pointers below are never touched)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4_calib.h")
+
+
+@pytest.fixture(scope="module")
+def C():
+    from fp4_precision_gemms_amd import calib
+    if not os.path.exists(calib.LIB_PATH):
+        pytest.skip("libfp4calib.so not built")
+    return calib
+
+
+def declared():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_declared_symbols_exported(C):
+    names = declared()
+    assert names == ["fp4_calib_mfma", "fp4_calib_mfma_flops", "fp4_calib_mfma_src_bytes"]
+    out = subprocess.check_output(["nm", "-D", "--defined-only", C.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_work_counts(C):
+    L = C.lib()
+    # 18 fragments of 16 bytes per lane, 256 lanes per workgroup
+    assert L.fp4_calib_mfma_src_bytes(256) == 256 * 256 * 18 * 16
+    assert L.fp4_calib_mfma_src_bytes(0) == 0
+    # 2*32*32*64 flop per MFMA, 28 MFMAs per wave-iteration, 4 waves
+    assert L.fp4_calib_mfma_flops(2, 3) == 2 * 32 * 32 * 64 * 28 * 3 * 2 * 4
+    assert L.fp4_calib_mfma_flops(0, 3) == 0.0
+
+
+def test_argument_errors(C):
+    L = C.lib()
+    A = 0x10000
+    assert L.fp4_calib_mfma(0, 1, 1, A, A, None) == 1
+    assert L.fp4_calib_mfma(A, 1, 1, 0, A, None) == 1
+    assert L.fp4_calib_mfma(A, 0, 1, A, A, None) == 2
+    assert L.fp4_calib_mfma(A, 65537, 1, A, A, None) == 2
+    assert L.fp4_calib_mfma(A, 1, 0, A, A, None) == 2
+    assert L.fp4_calib_mfma(A, 1, (1 << 24) + 1, A, A, None) == 2
+    assert L.fp4_calib_mfma(A + 8, 1, 1, A, A, None) == 3
