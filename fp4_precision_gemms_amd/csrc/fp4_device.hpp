@@ -70,24 +70,20 @@ __device__ __forceinline__ uint32_t e2m1_rtn(float v) {
 
 // Stochastic rounding with the comparator (u >> 8) * 2^-24 < p, p the
 // fractional position of |v| between its grid neighbours; |v| >= 6 gives 6.
+// Branch-free: the grid step is 0.5 below 2, 1 below 4 and 2 below 8, so
+// t = |v| / step (an exact power-of-two scaling) has integer part
+// code - 2k for the region k = 0, 1, 2 and fractional part p.  A NaN gives
+// code 6 (never reached from a block with a finite scale).
 __device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u) {
     const uint32_t bits = __float_as_uint(v);
     const uint32_t sign = (bits >> 28) & 8u;
     const float a = __uint_as_float(bits & 0x7FFFFFFFu);
     const float r = (float)(u >> 8) * 0x1p-24f;
-    uint32_t m;
-    if (a >= 6.0f) {
-        m = 7u;
-    } else if (a < 2.0f) {                           // step 0.5: lo = floor(2a)/2
-        const float t = a * 2.0f;
-        const float fl = __builtin_floorf(t);
-        m = (uint32_t)fl + (r < (t - fl) ? 1u : 0u);
-    } else if (a < 4.0f) {                           // step 1: grid 2, 3
-        const float fl = __builtin_floorf(a);
-        m = (uint32_t)fl + 2u + (r < (a - fl) ? 1u : 0u);   // 2 -> 4, 3 -> 5
-    } else {                                         // step 2: grid 4, 6
-        m = 6u + (r < (a - 4.0f) * 0.5f ? 1u : 0u);
-    }
+    const bool lo = a < 2.0f, mid = a < 4.0f;
+    const float t = a * (lo ? 2.0f : (mid ? 1.0f : 0.5f));
+    const float fl = __builtin_floorf(t);
+    uint32_t m = (uint32_t)fl + (lo ? 0u : (mid ? 2u : 4u)) + (r < t - fl ? 1u : 0u);
+    m = a < 6.0f ? m : (a >= 6.0f ? 7u : 6u);
     return sign | m;
 }
 
