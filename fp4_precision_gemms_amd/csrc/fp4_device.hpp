@@ -138,7 +138,9 @@ __device__ __forceinline__ uint32_t e4m3_sr(float a, uint32_t u) {
     if (a >= 448.0f) return 0x7Eu;
     float lo, gap;
     const uint32_t c = e4m3_floor(a, &lo, &gap);
-    const float p = (a - lo) / gap;                  // exact: gap is a power of two
+    // (a - lo) / gap as a product with the exact reciprocal of the power of
+    // two gap (2^-9 .. 2^5): the same binary32 result, without a division
+    const float p = (a - lo) * __uint_as_float((254u << 23) - __float_as_uint(gap));
     const float r = (float)(u >> 8) * 0x1p-24f;
     return r < p ? c + 1u : c;
 }

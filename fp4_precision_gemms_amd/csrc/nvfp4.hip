@@ -228,6 +228,107 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
     }
 }
 
+// Word (lane mod 4) of the four words lane U of this lane's quad holds:
+// four DPP quad broadcasts, then a select.
+template <int U>
+__device__ __forceinline__ uint32_t quad_word(const uint4& w, int wsel) {
+    constexpr int kBroadcast = 0x55 * U;        // quad_perm [U, U, U, U]
+    const uint32_t w0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w.x, kBroadcast, 0xF, 0xF, false);
+    const uint32_t w1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w.y, kBroadcast, 0xF, 0xF, false);
+    const uint32_t w2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w.z, kBroadcast, 0xF, 0xF, false);
+    const uint32_t w3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w.w, kBroadcast, 0xF, 0xF, false);
+    return wsel == 0 ? w0 : wsel == 1 ? w1 : wsel == 2 ? w2 : w3;
+}
+
+// The renormalized mode with one lane per block: wave w of the grid owns
+// blocks 256 w .. 256 w + 255, lane l of it blocks 256 w + 64 u + l for
+// u = 0..3 (two 16-byte loads per block, consecutive lanes on consecutive
+// blocks).  Each lane then rotates, scales, encodes and sums its whole block
+// -- the fmaf chains run over the 16 elements in order in one lane -- so the
+// per-block work (three divisions, E4M3 rounding) is done once per block.
+// The scale SR words: block blk takes word blk mod 4 of counter blk / 4, so
+// the four lanes of a quad need, for each u, the four words of one counter;
+// lane j of the quad draws the counter of u = j and DPP broadcasts within
+// the quad hand each lane its word.
+template <bool HAD>
+__global__ __launch_bounds__(kThreads) void nv_quant_renorm(
+    const uint4* __restrict__ x, int64_t nblocks, uint32_t sign_word, const float* __restrict__ amax_p,
+    uint64_t sr_seed, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ tensor_scale) {
+    const float amax = *amax_p;
+    const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;   // 6 * 448
+    const float six_st = 6.0f * s_t;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+    const int lane = threadIdx.x & 63;
+    const int64_t b0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 256;
+    uint4 wv[2 * kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t blk = b0 + 64 * u + lane;
+        const bool in = blk < nblocks;
+        wv[2 * u] = in ? x[2 * blk] : make_uint4(0, 0, 0, 0);
+        wv[2 * u + 1] = in ? x[2 * blk + 1] : make_uint4(0, 0, 0, 0);
+    }
+    // lane 4k + j: the counter of blocks b0 + 64 j + 4k .. + 3
+    const uint4 mine = stream4(sr_seed, 2u, (uint64_t)((b0 >> 2) + 16 * (lane & 3) + (lane >> 2)));
+    const int wsel = lane & 3;
+    static_assert(kUnroll == 4, "one quad lane per block slot");
+    const uint32_t srw[kUnroll] = {quad_word<0>(mine, wsel), quad_word<1>(mine, wsel),
+                                   quad_word<2>(mine, wsel), quad_word<3>(mine, wsel)};
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t blk = b0 + 64 * u + lane;
+        if (blk >= nblocks) break;                  // only the grid's last wave
+        float y[16];
+        const uint4 lo = wv[2 * u], hi = wv[2 * u + 1];
+        y[0] = bf16_lo(lo.x); y[1] = bf16_hi(lo.x); y[2] = bf16_lo(lo.y); y[3] = bf16_hi(lo.y);
+        y[4] = bf16_lo(lo.z); y[5] = bf16_hi(lo.z); y[6] = bf16_lo(lo.w); y[7] = bf16_hi(lo.w);
+        y[8] = bf16_lo(hi.x); y[9] = bf16_hi(hi.x); y[10] = bf16_lo(hi.y); y[11] = bf16_hi(hi.y);
+        y[12] = bf16_lo(hi.z); y[13] = bf16_hi(hi.z); y[14] = bf16_lo(hi.w); y[15] = bf16_hi(hi.w);
+        if constexpr (HAD) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) y[t] = flip_if(y[t], (sign_word >> t) & 1u);
+#pragma unroll
+            for (int hh = 1; hh < 16; hh <<= 1) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i & hh) continue;
+                    const float a = y[i], b = y[i + hh];
+                    y[i] = a + b;
+                    y[i + hh] = a - b;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) y[t] = y[t] * 0.25f;
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) m = max(m, __float_as_uint(y[t]) & 0x7FFFFFFFu);
+        const uint32_t sb = e4m3_rne(__uint_as_float(m) / six_st);
+        uint32_t c0 = 0, c1 = 0, stored = sb;
+        if (sb != 0u) {
+            const float inv = 1.0f / (e4m3_value(sb) * s_t);
+            float v[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) v[t] = y[t] * inv;
+            c0 = encode8_unit(v);
+            c1 = encode8_unit(v + 8);
+            float yq[16];
+            decode8(c0, yq);
+            decode8(c1, yq + 8);
+            float num = 0.0f, den = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                num = fmaf(y[t], y[t], num);
+                den = fmaf(y[t], yq[t], den);
+            }
+            if (den > 0.0f) stored = e4m3_sr(num / (s_t * den), srw[u]);
+        }
+        codes[blk] = make_uint2(c0, c1);
+        scales[blk] = (uint8_t)stored;
+    }
+}
+
 template <bool HAD>
 hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw, int mode,
                          uint64_t sr_seed, const float* amax_in, uint8_t* codes, uint8_t* scales,
@@ -245,9 +346,10 @@ hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw,
     }
     const int64_t qblocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
     if (mode == 1) {
-        hipLaunchKernelGGL((nv_quant<HAD, 1>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
-                           (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
-                           tensor_scale);
+        const int64_t nblocks = nchunks / 2, per_wg = (int64_t)(kThreads / 64) * 256;
+        hipLaunchKernelGGL((nv_quant_renorm<HAD>), dim3((unsigned)((nblocks + per_wg - 1) / per_wg)),
+                           dim3(kThreads), 0, st, (const uint4*)x, nblocks, sw, amax_p, sr_seed,
+                           (uint2*)codes, scales, tensor_scale);
     } else if (mode == 2) {
         hipLaunchKernelGGL((nv_quant<HAD, 2>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
                            (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,

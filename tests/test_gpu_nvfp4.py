@@ -40,7 +40,7 @@ def check(bits, had, seed, mode, sr_seed, amax_in=None, what=""):
 
 @pytest.mark.parametrize("had", [O.HAD_NONE, O.HAD_DET, O.HAD_SIGNED])
 @pytest.mark.parametrize("mode", [O.NV_RTN, O.NV_RENORM_SR, O.NV_ELEMENT_SR])
-@pytest.mark.parametrize("shape", [(64, 256), (3, 16), (130, 1040)])
+@pytest.mark.parametrize("shape", [(64, 256), (3, 16), (130, 1040), (7, 48), (5, 112)])
 def test_nvfp4_parity(had, mode, shape):
     rng = np.random.default_rng(shape[0] + shape[1])
     bits = bf16_bits(rng.standard_t(4, shape))
