@@ -8,11 +8,12 @@ both operands in one fp4_wgrad_quantize launch), then dW[N, K] = dY^T X on
 the scaled FP4 matrix cores, fp32 output.  Inputs
 are synthetic bf16 tensors resident in HBM before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload gate_up] [--no-cpu-baseline]
-                    [--copy-calibration]
+    python bench.py [--steps K] [--warmup W] [--workload gate_up|q_proj|down_proj]
+                    [--variant det-rtn|signed-rtn|signed-rtn-perstep|sr]
+                    [--no-cpu-baseline] [--copy-calibration]
     python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
     python bench.py --nvfp4                            (the secondary NVFP4 quantizer)
-    python bench.py --layer                            (the whole linear layer: three GEMMs)
+    python bench.py --layer [--workload W]             (the whole linear layer: three GEMMs)
     python bench.py --mfma-ceiling                     (only the MFMA-rate measurement aid)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
@@ -42,6 +43,18 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 METRIC = "MXFP4 Wgrad TFLOPS incl. Hadamard+quantize (8192×14336×4096); quantizer GB/s"
 COUNTERS = os.path.join(ROOT, "profiles", "gemm_mx_wgrad_gate_up_counters.json")
 GEMM_SRC = os.path.join(ROOT, "fp4_precision_gemms_amd", "csrc", "gemm_mx.hip")
+
+
+# Rotation and rounding of the Wgrad operands (the down_proj workload is
+# specified under three of them): (hadamard, per-step sign seed, rounding,
+# per-step SR seeds).  Per-step seeds change with the step index, as a
+# training loop would pass them.
+VARIANTS = {
+    "det-rtn": ("deterministic-32", False, "rtn"),
+    "signed-rtn": ("random-sign-32, fixed seed", False, "rtn"),
+    "signed-rtn-perstep": ("random-sign-32, seed = step", True, "rtn"),
+    "sr": ("none", False, "sr, seeds = step"),
+}
 
 
 def quant_bytes(elems: int) -> float:
@@ -133,17 +146,22 @@ def counter_summary(fetch_dir, write_dir):
     return 0
 
 
-def cpu_baseline(w, dY, X):
+def cpu_baseline(w, dY, X, variant="det-rtn"):
     """The oracle, untuned, on a bounded sample of the same Wgrad: the full
-    Hadamard-32 + MXFP4 quantization of dY and X along tokens, then 256 of
-    dW's rows by the binary64 oracle GEMM, scaled to all rows.  Returns the
-    JSON object."""
+    rotation + MXFP4 quantization of dY and X along tokens (the variant's
+    transform and rounding, step 0's seeds), then 256 of dW's rows by the
+    binary64 oracle GEMM, scaled to all rows.  Returns the JSON object."""
     import oracle as O
 
+    had_name, _, rnd_name = VARIANTS[variant]
+    had = {"deterministic-32": O.HAD_DET, "none": O.HAD_NONE}.get(had_name, O.HAD_SIGNED)
+    rnd = O.RND_SR if rnd_name.startswith("sr") else O.RND_RTN
+    sign_seed = 1000 if variant == "signed-rtn-perstep" else 7
+    seeds = (1, 2) if rnd == O.RND_SR else (0, 0)
     n = 256
     t0 = time.perf_counter()
-    aq, as_ = O.quant_mx(dY, O.AXIS_ROWS, 32, O.HAD_DET)
-    bq, bs = O.quant_mx(X, O.AXIS_ROWS, 32, O.HAD_DET)
+    aq, as_ = O.quant_mx(dY, O.AXIS_ROWS, 32, had, sign_seed, rnd, seeds[0])
+    bq, bs = O.quant_mx(X, O.AXIS_ROWS, 32, had, sign_seed, rnd, seeds[1])
     t1 = time.perf_counter()
     O.gemm_rows(aq, as_, bq, bs, 0, n)
     t2 = time.perf_counter()
@@ -151,10 +169,10 @@ def cpu_baseline(w, dY, X):
     flops = 2.0 * w.T * w.N * w.K
     return {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
             "kind": "oracle",
-            "sample": "Hadamard-32 + MXFP4 quantization of all of dY[%d x %d] and X[%d x %d] "
+            "sample": "rotation (%s) + MXFP4 quantization (%s) of all of dY[%d x %d] and X[%d x %d] "
                       "along tokens (%.1f s), then %d of %d dW rows by the binary64 oracle GEMM "
                       "(%.1f s), GEMM time scaled by rows to the full layer (%.0f s total)"
-                      % (w.T, w.N, w.T, w.K, t1 - t0, n, w.N, t2 - t1, t_full)}
+                      % (had_name, rnd_name, w.T, w.N, w.T, w.K, t1 - t0, n, w.N, t2 - t1, t_full)}
 
 
 def nvfp4_bench(args) -> int:
@@ -230,7 +248,7 @@ def layer_bench(args) -> int:
     import fp4_precision_gemms_amd as F
     import workloads as W
 
-    w = W.WORKLOADS["gate_up"]
+    w = W.WORKLOADS[args.workload]
     T, N, K = w.T, w.N, w.K
     dev = torch.device("cuda:0")
     up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -290,11 +308,11 @@ def layer_bench(args) -> int:
             breakdown[name + "_TFLOPs"] = flop / (us * 1e-6) / 1e12
     gemm_us = min(per["fprop"], per["dgrad"], per["wgrad"])
     print(json.dumps({
-        "metric": "MXFP4 linear layer TFLOP/s (Fprop + Dgrad + Wgrad incl. dual quantization, 8192x14336x4096)",
+        "metric": "MXFP4 linear layer TFLOP/s (Fprop + Dgrad + Wgrad incl. dual quantization, %dx%dx%d)" % (T, N, K),
         "value": 3 * flop / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": "gate_up linear layer, all three GEMMs", "T": T, "N": N, "K": K,
+        "config": {"workload": "%s linear layer, all three GEMMs" % w.name, "T": T, "N": N, "K": K,
                    "hadamard": "deterministic-32 on the Wgrad operands", "rounding": "rtn",
                    "outputs": "fp32"},
         "roofline": {"bound": "mfma", "kernel": "gemm_mx_tn (fastest of the three roles)",
@@ -312,7 +330,9 @@ def main() -> int:
     # 100 warm-up steps (about 35 ms) then 100 timed steps
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="gate_up")
+    ap.add_argument("--workload", default="gate_up", choices=["gate_up", "q_proj", "down_proj"])
+    ap.add_argument("--variant", default="det-rtn", choices=sorted(VARIANTS),
+                    help="rotation and rounding of the Wgrad operands")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
@@ -371,11 +391,20 @@ def main() -> int:
     dw = torch.empty((N, K), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    had_name, per_step_sign, rnd_name = VARIANTS[args.variant]
+    had = {"deterministic-32": F.HAD_DET, "none": F.HAD_NONE}.get(had_name, F.HAD_SIGNED)
+    rnd = F.SR if rnd_name.startswith("sr") else F.RTN
+    counter = [0]
+
     def step(ev=None):
         # both Wgrad operands (one rotation, one launch), then the GEMM
+        i = counter[0]
+        counter[0] += 1
+        sign_seed = 1000 + i if per_step_sign else 7
+        sr_dy, sr_x = (2 * i + 1, 2 * i + 2) if rnd == F.SR else (0, 0)
         if ev is not None:
             ev[0].record(stream)
-        F.fp4_wgrad_quantize(dY, X, 32, F.HAD_DET, 0, F.RTN, 0, 0, out=(dytq, dyts, xtq, xts))
+        F.fp4_wgrad_quantize(dY, X, 32, had, sign_seed, rnd, sr_dy, sr_x, out=(dytq, dyts, xtq, xts))
         if ev is not None:
             ev[1].record(stream)
         F.fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=dw)
@@ -410,7 +439,8 @@ def main() -> int:
     q_gbs = (quant_bytes(T * N) + quant_bytes(T * K)) / (t_q * 1e-3) / 1e9
     traffic = traffic_per_launch()
     out = {
-        "metric": METRIC,
+        "metric": METRIC if (w.name, args.variant) == ("gate_up", "det-rtn") else
+                  "MXFP4 Wgrad TFLOPS incl. rotation+quantize (%dx%dx%d, %s)" % (T, N, K, args.variant),
         "value": flops / (ms_step * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -422,9 +452,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": "%s Wgrad incl. Hadamard-32 + MXFP4 quantize" % w.name,
-                   "T": T, "N": N, "K": K, "hadamard": "deterministic-32 along tokens",
-                   "rounding": "rtn", "output": "fp32 dW[N,K]"},
+        "config": {"workload": "%s Wgrad incl. rotation + MXFP4 quantize" % w.name,
+                   "T": T, "N": N, "K": K, "hadamard": had_name + " along tokens",
+                   "rounding": rnd_name, "output": "fp32 dW[N,K]"},
         "roofline": {"bound": "mfma", "kernel": "gemm_mx_tn (Wgrad)",
                      "achieved": gemm_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / MXFP4_PEAK_TFLOPS, "traffic": traffic},
@@ -441,7 +471,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, dY_np, X_np)
+        out["cpu_baseline"] = cpu_baseline(w, dY_np, X_np, args.variant)
     print(json.dumps(out), flush=True)
     return 0
 
