@@ -159,14 +159,22 @@ def fp4_wgrad_quantize(dy: torch.Tensor, x: torch.Tensor, had_n: int = 32, had: 
                        out=None, stream=None):
     """The Wgrad operand pair: dY[T, N] and X[T, K] quantized along T with one
     rotation; returns (dytq, dyts, xtq, xts) (see include/fp4.h)."""
-    _need(dy, torch.bfloat16, "dy")
-    _need(x, torch.bfloat16, "x")
     T, N = dy.shape
     if x.shape[0] != T:
         raise ValueError("dy and x must have the same number of rows")
     K = x.shape[1]
+    (a, b), (c, d) = mx_shapes(T, N, AXIS_ROWS), mx_shapes(T, K, AXIS_ROWS)
+    if out is not None:
+        # the kernels write exactly these extents: a smaller buffer would be
+        # written past its end
+        if len(out) != 4:
+            raise ValueError("out must be (dytq, dyts, xtq, xts)")
+        for t, sh, n in zip(out, (a, b, c, d), ("dytq", "dyts", "xtq", "xts")):
+            if tuple(t.shape) != tuple(sh):
+                raise ValueError("%s must have shape %s, got %s" % (n, tuple(sh), tuple(t.shape)))
+    _need(dy, torch.bfloat16, "dy")
+    _need(x, torch.bfloat16, "x")
     if out is None:
-        (a, b), (c, d) = mx_shapes(T, N, AXIS_ROWS), mx_shapes(T, K, AXIS_ROWS)
         out = tuple(torch.empty(sh, dtype=torch.uint8, device=dy.device) for sh in (a, b, c, d))
     for t in out:
         _need(t, torch.uint8, "output")
@@ -256,12 +264,25 @@ def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, m
                    workspace: torch.Tensor | None = None, stream=None):
     """NVFP4 codes [rows, cols/2], E4M3 scales [rows, cols/16] and the fp32
     tensor scale (a 1-element device tensor) of bf16 x (see include/fp4.h)."""
-    _need(x, torch.bfloat16, "x")
     rows, cols = x.shape
+    for t, sh, n in ((codes, (rows, cols // 2), "codes"), (scales, (rows, cols // 16), "scales"),
+                     (tensor_scale, (1,), "tensor_scale")):
+        if t is not None and tuple(t.shape) != sh:
+            raise ValueError("%s must have shape %s, got %s" % (n, sh, tuple(t.shape)))
+    if amax_in is not None and amax_in.numel() != 1:
+        raise ValueError("amax_in must hold one float")
+    _need(x, torch.bfloat16, "x")
     dev = x.device
     codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if codes is None else codes
     scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev) if scales is None else scales
     tensor_scale = torch.empty(1, dtype=torch.float32, device=dev) if tensor_scale is None else tensor_scale
+    for t, dt, n in ((codes, torch.uint8, "codes"), (scales, torch.uint8, "scales"),
+                     (tensor_scale, torch.float32, "tensor_scale")):
+        _need(t, dt, n)
+    if amax_in is not None:
+        _need(amax_in, torch.float32, "amax_in")
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
     if amax_in is None and workspace is None:
         workspace = torch.empty(nvfp4_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
     _check(lib().nvfp4_quantize(x.data_ptr(), rows, cols, had, sign_seed & (2 ** 64 - 1), mode,

@@ -203,3 +203,28 @@ def test_grouped_scale_layout_helpers():
     assert F.mx_shapes(64, 416, F.AXIS_COLS) == ((64, 208), (2, 64, 8))
     assert F.mx_shapes(416, 64, F.AXIS_ROWS) == ((64, 208), (2, 64, 8))
     assert F.mx_shapes(3, 256, F.AXIS_COLS)[1] == (1, 3, 8)
+
+
+def test_binding_checks_output_extents():
+    """Outputs that the kernels would write past the end of are refused
+    before any launch (the shape checks come before the device checks)."""
+    import torch
+    T, N, K = 64, 96, 32
+    dy, x = torch.zeros(T, N, dtype=torch.bfloat16), torch.zeros(T, K, dtype=torch.bfloat16)
+    (a, b), (c, d) = F.mx_shapes(T, N, F.AXIS_ROWS), F.mx_shapes(T, K, F.AXIS_ROWS)
+    u8 = lambda sh: torch.zeros(sh, dtype=torch.uint8)
+    # the two operands' buffers swapped: dY's outputs too small
+    with pytest.raises(ValueError, match="shape"):
+        F.fp4_wgrad_quantize(dy, x, out=(u8(c), u8(d), u8(a), u8(b)))
+    with pytest.raises(ValueError, match="out must be"):
+        F.fp4_wgrad_quantize(dy, x, out=(u8(a), u8(b), u8(c)))
+    xn = torch.zeros(32, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="codes must have shape"):
+        F.nvfp4_quantize(xn, codes=u8((32, 16)))
+    with pytest.raises(ValueError, match="scales must have shape"):
+        F.nvfp4_quantize(xn, scales=u8((32, 2)))
+    with pytest.raises(ValueError, match="tensor_scale"):
+        F.nvfp4_quantize(xn, tensor_scale=torch.zeros(2))
+    # right extents on CPU tensors: refused as not on the GPU, not for shape
+    with pytest.raises(ValueError, match="GPU"):
+        F.fp4_wgrad_quantize(dy, x, out=(u8(a), u8(b), u8(c), u8(d)))
