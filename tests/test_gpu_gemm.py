@@ -132,9 +132,10 @@ def test_gemm_full_size_sampled(wname):
 # Shapes on which the tile-shape choice (least rounds x tile area on 256 CUs)
 # takes each of the kernel's tile shapes: 256 x 256 (4096 x 4096), 224 x 256
 # (14336 x 4096, the Wgrad gate/up output) and 256 x 224 (4096 x 14336), with
-# ragged edges and contraction sizes with and without a partial last stage.
+# ragged edges and contraction sizes with and without a partial last stage
+# (640 and 384: 256 x 256 tiles with a half-empty last stage).
 TILE_SHAPES = [(4096, 4096, 512), (4000, 4090, 288), (14336, 4096, 256), (14300, 4000, 320),
-               (4096, 14336, 256), (4090, 14300, 96)]
+               (4096, 14336, 256), (4090, 14300, 96), (4096, 4090, 640), (4000, 4096, 384)]
 
 
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
