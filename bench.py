@@ -14,6 +14,7 @@ are synthetic bf16 tensors resident in HBM before timing starts.
     python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
     python bench.py --nvfp4                            (the secondary NVFP4 quantizer)
     python bench.py --layer [--workload W]             (the whole linear layer: three GEMMs)
+    python bench.py --autograd [--workload W]          (MXFP4LinearFunction forward + backward, bf16)
     python bench.py --mfma-ceiling                     (only the MFMA-rate measurement aid)
 
 Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
@@ -323,6 +324,55 @@ def layer_bench(args) -> int:
     return 0
 
 
+def autograd_bench(args) -> int:
+    """The linear layer as training uses it: MXFP4LinearFunction forward
+    (Y = X W^T) and backward (dX, dW) through torch autograd on the
+    workload's shapes, bf16 inputs and outputs, deterministic Hadamard-32 on
+    the Wgrad operands, RTN.  A step = forward + backward with a fixed
+    upstream gradient dY; 3 * 2 T N K flops per step.  One JSON line."""
+    import numpy as np
+    import torch
+
+    from fp4_precision_gemms_amd.linear import MXFP4LinearFunction
+    import fp4_precision_gemms_amd as F
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    T, N, K = w.T, w.N, w.K
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = up(W.tensor(w, "X")).requires_grad_(True)
+    wt = up(W.tensor(w, "W")).requires_grad_(True)
+    dy = up(W.tensor(w, "dY"))
+
+    def step():
+        y = MXFP4LinearFunction.apply(x, wt, F.HAD_DET, 32, 0, F.RTN, 0)
+        x.grad = None
+        wt.grad = None
+        y.backward(dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / args.steps
+    flop = 3 * 2.0 * T * N * K
+    print(json.dumps({
+        "metric": "MXFP4 linear layer training step TFLOP/s (autograd forward + backward, %dx%dx%d)" % (T, N, K),
+        "value": flop / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "%s MXFP4LinearFunction forward + backward" % w.name, "T": T, "N": N, "K": K,
+                   "hadamard": "deterministic-32 on the Wgrad operands", "rounding": "rtn",
+                   "outputs": "bf16 Y, dX, dW"}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +390,8 @@ def main() -> int:
                     help="summarize two rocprofv3 counter runs and exit")
     ap.add_argument("--nvfp4", action="store_true", help="time the NVFP4 quantizer instead")
     ap.add_argument("--layer", action="store_true", help="time the whole linear layer instead")
+    ap.add_argument("--autograd", action="store_true",
+                    help="time MXFP4LinearFunction forward + backward instead")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the MFMA-only rate on random operands (libfp4calib.so)")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
@@ -356,6 +408,8 @@ def main() -> int:
         return nvfp4_bench(args)
     if args.layer:
         return layer_bench(args)
+    if args.autograd:
+        return autograd_bench(args)
     if args.mfma_ceiling:
         import torch
         from fp4_precision_gemms_amd import calib
