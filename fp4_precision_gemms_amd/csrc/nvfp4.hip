@@ -16,15 +16,18 @@
 //   nv_amax  -- rotate each 16-block (pairs of lanes, 8 elements each) and
 //               reduce max |y| into one workspace word (atomic max on the
 //               float bits, valid because every value is non-negative);
-//   nv_quant -- rotate again, derive s_t from the amax, per block the E4M3
-//               scale, the E2M1 codes and, with renorm, the scale rounded
-//               stochastically toward |y|^2 / (s_t sum y_i q_i).  The codes
-//               come from the hardware FP4 conversion of fl(y_i * inv) with
-//               scale 1 (round to nearest even, saturating -- the rule the
-//               MX quantizers check bit-exact), q_i from its inverse; in the
-//               element-SR mode from the MX quantizers' stochastic rounding
-//               with the element stream (purpose 0, index = row-major
-//               position: two Philox calls per 8-element chunk).
+//   nv_quant_renorm (renormalized scales) -- one lane per block: rotate
+//               again, derive s_t from the amax, the block's E4M3 scale, the
+//               E2M1 codes and the scale rounded stochastically toward
+//               |y|^2 / (s_t sum y_i q_i);
+//   nv_quant (elements to nearest, or every element stochastically) -- a
+//               lane pair per block.
+// Codes to nearest come from the hardware FP4 conversion of fl(y_i * inv)
+// with scale 1 (round to nearest even, saturating -- the rule the MX
+// quantizers check bit-exact), q_i from its inverse; in the element-SR mode
+// from the MX quantizers' stochastic rounding with the element stream
+// (purpose 0, index = row-major position: two Philox calls per 8-element
+// chunk).
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
@@ -32,9 +35,8 @@ namespace fp4dev {
 namespace {
 
 constexpr int kThreads = 256;
-// 16-byte chunks per thread: in nv_quant the upper halves (or lower) of 4
-// consecutive 16-element blocks, so one Philox call gives the 4 blocks'
-// scale SR words; in nv_amax 4 independent loads in flight.
+// Loads in flight per thread: 16-byte chunks in nv_amax and nv_quant, whole
+// blocks in nv_quant_renorm (four per lane, the four words of a Philox call).
 constexpr int kUnroll = 4;
 // Workgroups of the amax pass (each ends with one atomic max on the same
 // word: 8192 of them serialized behind each other cost 2x the pass).
@@ -139,26 +141,23 @@ __device__ __forceinline__ void decode8(uint32_t w, float* out) {
     r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); out[6] = r.x; out[7] = r.y;
 }
 
-// MODE 0: RTN; 1: RTN + renormalized scale by SR; 2: element SR.
+// MODE 0: RTN; 2: element SR (the renormalized mode is nv_quant_renorm).
 template <bool HAD, int MODE>
 __global__ __launch_bounds__(kThreads) void nv_quant(
     const uint4* __restrict__ x, int64_t nchunks, uint32_t sign_word, const float* __restrict__ amax_p,
     uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tensor_scale) {
+    static_assert(MODE == 0 || MODE == 2, "RTN or element SR");
     const float amax = *amax_p;
-    constexpr bool RENORM = MODE == 1;
     const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;   // 6 * 448
     const float six_st = 6.0f * s_t;
     if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
     const int q = threadIdx.x & 1;
-    // With renorm, lane pair p (lanes 2p, 2p+1 of the grid) owns blocks
-    // 4p .. 4p+3, one 8-element half of each per lane (chunk 2 blk + q), so
-    // that one Philox call serves all four; without, chunk u of a thread is
-    // kThreads chunks after chunk u - 1 (every load instruction contiguous).
-    // All chunks are loaded first.
-    const int64_t pair = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 1;
+    // Lanes 2p, 2p+1 hold the two 8-element halves of one block; chunk u of
+    // a thread is kThreads chunks after chunk u - 1 (every load instruction
+    // contiguous).  All chunks are loaded first.
     auto chunk = [&](int u) -> int64_t {
-        return RENORM ? 8 * pair + 2 * u + q : ((int64_t)blockIdx.x * kUnroll + u) * kThreads + threadIdx.x;
+        return ((int64_t)blockIdx.x * kUnroll + u) * kThreads + threadIdx.x;
     };
     uint4 wv[kUnroll];
 #pragma unroll
@@ -166,9 +165,6 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
         const int64_t g = chunk(u);
         wv[u] = g < nchunks ? x[g] : make_uint4(0, 0, 0, 0);
     }
-    // scale SR words of the 4 blocks: word u of counter (blk >> 2) = p
-    uint4 srw = make_uint4(0, 0, 0, 0);
-    if constexpr (RENORM) srw = stream4(sr_seed, 2u, (uint64_t)pair);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t g = chunk(u);
@@ -180,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
         for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(y[t]) & 0x7FFFFFFFu);
         m = max(m, pair_xor1(m));
         const uint32_t sb = e4m3_rne(__uint_as_float(m) / six_st);
-        uint32_t word = 0, stored = sb;
+        uint32_t word = 0;
         if (sb != 0u) {
             const float inv = 1.0f / (e4m3_value(sb) * s_t);
             float v[8];
@@ -196,35 +192,9 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
             } else {
                 word = encode8_unit(v);
             }
-            if constexpr (RENORM) {
-                // sequential binary32 fmaf chains over the 16 elements in order:
-                // the lower lane's partial sums seed the upper lane's chain
-                float yq[8];
-                decode8(word, yq);
-                float num = 0.0f, den = 0.0f;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    num = fmaf(y[t], y[t], num);
-                    den = fmaf(y[t], yq[t], den);
-                }
-                float pnum = pair_xor1f(num), pden = pair_xor1f(den);
-                if (q) {
-                    num = pnum;
-                    den = pden;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        num = fmaf(y[t], y[t], num);
-                        den = fmaf(y[t], yq[t], den);
-                    }
-                    if (den > 0.0f) {
-                        const float target = num / (s_t * den);
-                        stored = e4m3_sr(target, word_of(srw, u));
-                    }
-                }
-            }
         }
         codes[g] = word;
-        if (q == 1) scales[g >> 1] = (uint8_t)stored;
+        if (q == 1) scales[g >> 1] = (uint8_t)sb;
     }
 }
 
