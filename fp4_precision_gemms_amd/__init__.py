@@ -97,12 +97,38 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
+def code_shape(R: int, C: int):
+    """Shape of the MXFP4 codes of R rows of C contraction elements in the
+    library's 32-row tiled layout: for each group of 32 rows and each
+    32-element block, the 32 rows' 16 code bytes are one 512-byte chunk
+    ([ceil(R/32), C/32, 512]; row r at bytes 16 (r mod 32) of its chunk)."""
+    return ((R + 31) // 32, C // 32, 512)
+
+
+def scale_shape(R: int, C: int):
+    """k-grouped E8M0 scale shape of R rows of C contraction elements:
+    [ceil(C/256), R, 8], block b of row r at [b // 8, r, b % 8]."""
+    return ((C // 32 + 7) // 8, R, 8)
+
+
 def mx_shapes(rows: int, cols: int, axis: int):
-    """(codes shape, scales shape) of fp4_hadamard_quantize's outputs: codes
-    [R, C/2]; scales k-grouped, [ceil(C/256), R, 8] (block b of row r at
-    [b // 8, r, b % 8])."""
+    """(codes shape, scales shape) of fp4_hadamard_quantize's outputs for
+    x[rows, cols] along `axis` (the logical operand has R rows of C
+    contraction elements: (rows, cols) along cols, (cols, rows) along rows)."""
     R, C = (rows, cols) if axis == AXIS_COLS else (cols, rows)
-    return (R, C // 2), ((C // 32 + 7) // 8, R, 8)
+    return code_shape(R, C), scale_shape(R, C)
+
+
+def mx_dims(codes: torch.Tensor, scales: torch.Tensor):
+    """(R, C) of an MXFP4 operand from its codes and scales, checking that
+    the two agree."""
+    if codes.dim() != 3 or scales.dim() != 3:
+        raise ValueError("MXFP4 operands are codes [ceil(R/32), C/32, 512] and scales [ceil(C/256), R, 8]")
+    R, C = scales.shape[1], codes.shape[1] * 32
+    if tuple(codes.shape) != code_shape(R, C) or tuple(scales.shape) != scale_shape(R, C):
+        raise ValueError("codes %s and scales %s do not describe one operand"
+                         % (tuple(codes.shape), tuple(scales.shape)))
+    return R, C
 
 
 def fp4_hadamard_quantize(x: torch.Tensor, axis: int = AXIS_COLS, had_n: int = 32,
@@ -198,42 +224,38 @@ def _gemm(fn, aq, as_, bq, bs, T, N, K, out_shape, out, stream):
     return out
 
 
-def _sshape(R: int, C: int):
-    """k-grouped scale shape of R rows of C contraction elements."""
-    return ((C // 32 + 7) // 8, R, 8)
+def _operands(aq, as_, bq, bs, what):
+    M, Ka = mx_dims(aq, as_)
+    N, Kb = mx_dims(bq, bs)
+    if Ka != Kb:
+        raise ValueError("%s operands have different contraction sizes (%d, %d)" % (what, Ka, Kb))
+    return M, N, Ka
 
 
 def fp4_gemm_fprop(xq, xs, wq, ws, out=None, stream=None):
-    """y[T, N] = X W^T from xq [T, K/2] and wq [N, K/2] (both blocked along K)."""
-    T, K, N = xq.shape[0], xq.shape[1] * 2, wq.shape[0]
-    if wq.shape[1] * 2 != K or tuple(xs.shape) != _sshape(T, K) or tuple(ws.shape) != _sshape(N, K):
-        raise ValueError("fprop operand shapes disagree")
+    """y[T, N] = X W^T from X and W quantized along K."""
+    T, N, K = _operands(xq, xs, wq, ws, "fprop")
     return _gemm(lib().fp4_gemm_fprop, xq, xs, wq, ws, T, N, K, (T, N), out, stream)
 
 
 def fp4_gemm_dgrad(dyq, dys, wtq, wts, out=None, stream=None):
-    """dx[T, K] = dY W from dyq [T, N/2] (blocked along N) and wtq [K, N/2]."""
-    T, N, K = dyq.shape[0], dyq.shape[1] * 2, wtq.shape[0]
-    if wtq.shape[1] * 2 != N or tuple(dys.shape) != _sshape(T, N) or tuple(wts.shape) != _sshape(K, N):
-        raise ValueError("dgrad operand shapes disagree")
+    """dx[T, K] = dY W from dY quantized along N and W^T (W along its rows)."""
+    T, K, N = _operands(dyq, dys, wtq, wts, "dgrad")
     return _gemm(lib().fp4_gemm_dgrad, dyq, dys, wtq, wts, T, N, K, (T, K), out, stream)
 
 
 def fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=None, stream=None):
-    """dw[N, K] = dY^T X from dytq [N, T/2] and xtq [K, T/2] (blocked along T)."""
-    N, T, K = dytq.shape[0], dytq.shape[1] * 2, xtq.shape[0]
-    if xtq.shape[1] * 2 != T or tuple(dyts.shape) != _sshape(N, T) or tuple(xts.shape) != _sshape(K, T):
-        raise ValueError("wgrad operand shapes disagree")
+    """dw[N, K] = dY^T X from dY^T and X^T (both quantized along T)."""
+    N, K, T = _operands(dytq, dyts, xtq, xts, "wgrad")
     return _gemm(lib().fp4_gemm_wgrad, dytq, dyts, xtq, xts, T, N, K, (N, K), out, stream)
 
 
 def fp4_gemm_mx(aq, as_, bq, bs, out=None, out_dtype: int = OUT_F32, accumulate: bool = False,
                 stream=None):
-    """C[M, N] = A B^T (+ C when accumulate) from aq [M, Kc/2] and bq [N, Kc/2]
-    (both blocked along Kc); C fp32 or bf16 (see include/fp4.h)."""
-    M, Kc, N = aq.shape[0], aq.shape[1] * 2, bq.shape[0]
-    if bq.shape[1] * 2 != Kc or tuple(as_.shape) != _sshape(M, Kc) or tuple(bs.shape) != _sshape(N, Kc):
-        raise ValueError("operand shapes disagree")
+    """C[M, N] = A B^T (+ C when accumulate) from MXFP4 operands A [M, Kc] and
+    B [N, Kc] (codes and scales as the quantizers write them); C fp32 or
+    bf16 (see include/fp4.h)."""
+    M, N, Kc = _operands(aq, as_, bq, bs, "gemm")
     for t, n in ((aq, "a codes"), (as_, "a scales"), (bq, "b codes"), (bs, "b scales")):
         _need(t, torch.uint8, n)
     dt = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16}[out_dtype]

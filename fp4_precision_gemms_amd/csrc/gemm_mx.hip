@@ -5,52 +5,49 @@
 // нестабильности": the three GEMMs of a linear layer (Fprop, Dgrad, Wgrad)
 // run in MXFP4 on native FP4 matrix cores.  All three are one "TN" product
 //     C[m, n] = sum_k a[m, k] b[n, k]
-// of two operands stored along their contraction axis as E2M1 codes (two per
-// byte, even k in the low nibble) with one E8M0 scale per 32 k.  The scales
-// of an operand with R rows are k-grouped: the 8 bytes of blocks 8g .. 8g+7
-// of row r sit at (g R + r) * 8, so the scales of one 256-k stage of
-// consecutive rows are one contiguous run.
+// of two operands stored along their contraction axis as E2M1 codes with one
+// E8M0 scale per 32 k.
 //
-// Kernel layout (WM x WN waves of 64 lanes -- 4 in the shapes launched,
-// 2 x 2 for 256 x 256, 1 x 4 for 224 x 256, 4 x 1 for 256 x 224; the
-// template also builds 8 -- block tile BM x BN, wave tile BM/WM x BN/WN made
-// of 32 x 32 MFMA tiles):
-//   - V_MFMA_SCALE_F32_32X32X64_F8F6F4 with both operands FP4 (format 4) and
-//     fp32 accumulation.  Operand lane l supplies row (l mod 32) and k-half
-//     (l div 32) of a 32 x 64 slice: 32 consecutive k = one 16-byte code
-//     chunk = exactly one scale block, so the lane's scale byte is that
-//     block's E8M0 scale.  The B tile is passed as the instruction's first
-//     operand, so the accumulator holds C^T: lane l owns row m = l mod 32 of
-//     C and four runs of four consecutive n, each stored as one 16-byte write.
-//   - A stage is BK = 256 k: 128 code bytes and one 8-byte scale group per
-//     row.  Both go global -> LDS by buffer_load ... lds (no VGPR round trip) into a
-//     ring of NBUF stage buffers, NBUF - 1 stages ahead of the MFMAs.  One
-//     dwordx4 instruction fills 64 16-byte slots of consecutive rows, lane i
-//     writing slot i; the lane fetches the chunk that belongs in that slot.
-//     Chunk c of row r sits in slot c XOR ((r / (16 / CPR)) mod CPR), CPR the
-//     chunks per row: the 16 lanes the LDS serves per clock (rows r..r+15 of
-//     one chunk) then hit all 64 banks once.  A dword instruction copies the
-//     contiguous scale groups of 32 rows.  Rows past M (or N) lie outside
-//     the buffer range and read as zero.
-//   - Per stage a wave issues the DMA of stage kt + NBUF - 1 and the fragment
-//     reads of its k-steps 1.. between the MFMAs of its k-steps 0.., then
-//     waits for its own DMA of stage kt + 1; one barrier makes that stage
-//     visible to all waves and frees buffer kt; the scales and k-step 0
-//     fragments of stage kt + 1 are read while the last k-step's MFMAs run.
-//   - A contraction that is not a multiple of BK (KTAIL) zero-fills the
-//     missing code chunks through out-of-range offsets and loads the scales
-//     through registers with the blocks past the end set to 127.
+// Operand layouts (written so by the quantizers):
+//   - codes, "32-row tiled": for each group of 32 rows and each 32-element
+//     block, the 32 rows' 16 code bytes (two per byte, even k in the low
+//     nibble) are one contiguous 512-byte chunk, row r of the group at
+//     16 * (r mod 32); chunk (g, b) of an operand with nb blocks per row sits
+//     at (g * nb + b) * 512.  Two consecutive chunks of a row group are then
+//     exactly the 1 KB operand of one 32 x 32 x 64 MFMA k-step in lane order.
+//   - scales, k-grouped: the 8 bytes of blocks 8q .. 8q+7 of row r at
+//     (q R + r) * 8, so one 256-k stage of consecutive rows is one run.
+//
+// Kernel (one workgroup of 4 waves per CU, persistent over tiles):
+//   - block tile BM x 256 (BM = 32 FM, FM = 7 or 8), wave w computes all BM
+//     rows x columns 64 w .. 64 w + 63 with V_MFMA_SCALE_F32_32X32X64_F8F6F4
+//     (FP4 x FP4, fp32 accumulation).  The B operand is the instruction's
+//     first source, so an accumulator holds a 32 x 32 tile of C^T: lane l
+//     owns row m = l mod 32 and four runs of four consecutive n.
+//   - A (shared by the four waves) goes global -> LDS by buffer_load ... lds
+//     into a ring of four 256-k stage slots; the DMA of stage kt + 3 is
+//     spread over the k-steps of stage kt, and the wait for a stage is issued
+//     two stages after its DMA.  Measured on this chip: issuing a stage's DMA
+//     in one burst stalls the in-order MFMA issue behind the per-CU load
+//     path, and a wait one stage after the issue exposes the load latency.
+//   - B (private to each wave: its 64 rows) goes global -> registers: each
+//     k-step's two 1 KB fragments are one contiguous load each (the tiled
+//     layout), issued 8 k-steps ahead into a register ring; B scales come
+//     from HBM one stage group per load, two stages ahead.
+//   - A contraction that is not a multiple of 256 (KTAIL) zero-fills chunks
+//     past the end through out-of-range buffer offsets and sets the scale
+//     bytes of blocks past the end to 127 (2^0).
 //   - Block order: workgroups are dispatched round-robin over the 8 XCDs;
-//     the block index is remapped so that each XCD works on a contiguous run
-//     of tiles, ordered in groups of GM tile-rows, so tiles that share A and
-//     B rows meet in the same L2.
-//   - Persistent workgroups (one per CU) loop over their tiles.  The output
-//     leaves through LDS in whole rows per store instruction; when a tile and
-//     the workgroup's next tile are both full, the next tile's first stage is
-//     issued before the epilogue (into stage buffer 0, the epilogue staging
-//     in buffer 1), so its latency hides behind the stores.
+//     the tile index is remapped so that each XCD works on a contiguous run
+//     of tiles, ordered in groups of GM tile-rows.
+//   - Epilogue: each wave stages 32 rows of its 64 columns at a time in one
+//     LDS slot and stores whole rows per instruction.  When the tile and the
+//     workgroup's next tile are both full, the next tile's first stages are
+//     issued before the epilogue (into the other three slots).
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
+
+#include <atomic>
 
 namespace fp4dev {
 namespace {
@@ -58,10 +55,12 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kXcds = 8;
 constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr uint32_t kOob = 0x80000000u;     // a buffer offset past any range: reads zero
 
 // s_waitcnt immediate: vmcnt(n) with lgkmcnt(0).
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
@@ -114,17 +113,14 @@ __device__ __forceinline__ void tile_of_block(int b, int nb, int tm, int tn, int
     tile_n = r / gm;
 }
 
-// Scale word w (bytes 4w .. 4w+3 of group kt) of one row of an operand with
-// R rows and ks blocks per row, k-grouped; blocks at or past ks (the unused
-// tail of the last group) read as 127 (2^0; their codes are zero).
-__device__ __forceinline__ uint32_t scale_word_masked(const uint8_t* __restrict__ S, int64_t R,
-                                                      int64_t row, int64_t ks, int kt, int w) {
-    const int64_t b0 = (int64_t)kt * 8 + 4 * w;
-    const uint8_t* p = S + ((int64_t)kt * R + row) * 8 + 4 * w;
-    uint32_t word = 0;
+// Bytes of a scale word for blocks first .. first+3 that lie at or past nb
+// (the unused tail of the last k-group) set to 127 (2^0; their codes are
+// zero).
+__device__ __forceinline__ uint32_t mask_scale_word(uint32_t w, int64_t first, int64_t nb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) word |= (b0 + i < ks ? (uint32_t)p[i] : 127u) << (8 * i);
-    return word;
+    for (int i = 0; i < 4; ++i)
+        if (first + i >= nb) w = (w & ~(0xFFu << (8 * i))) | (127u << (8 * i));
+    return w;
 }
 
 // Round-to-nearest-even binary32 -> bfloat16 (NaN -> the quiet NaN 0x7FC0).
@@ -137,418 +133,444 @@ __device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float
 
 // A 16-byte store of C marked non-temporal: with whole 128-byte lines per
 // instruction the output streams to HBM during the GEMM instead of sitting
-// dirty in the caches until the next kernel's traffic evicts it (measured:
-// the quantizer that follows ran 14 us longer on dY[8192x14336]).  Partial
+// dirty in the caches until the next kernel's traffic evicts it.  Partial
 // lines must not take this path: non-temporal 16-byte pieces of a line are
 // written to memory one by one.
-typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_c_line_part(float* p, float4 v) {
     __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f*>(p));
 }
 
+constexpr int kWaves = 4, kThreads = 64 * kWaves;
+constexpr int kBN = 256;            // tile columns: 64 per wave
+constexpr int kKS = 4;              // MFMA k-steps (64 k each) per 256-k stage
+constexpr int kSlots = 4;           // A stage ring
+constexpr int kRing = 8;            // B register ring depth, in k-steps
+constexpr int kEpiRow = 64 * 4 + 16;            // a staged row of a wave's 64 fp32 columns, padded
+constexpr int kEpiRegion = 32 * kEpiRow;        // 32 rows per wave
+
 // OBF16: C is bfloat16 (else fp32); ACC: C = A B^T + C (else C = A B^T), the
-// sum formed in fp32 before the output rounding.
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool KTAIL, bool OBF16, bool ACC>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
+// sum formed in fp32 before the output rounding.  FAST: every tile is full
+// and the contraction is a multiple of 1024 (the stage count a multiple of
+// the ring), so no lane ever reads out of range; the prefetches past the
+// last stage re-load the last stage (never read) and each stage's offset is
+// a scalar added to per-tile descriptors.
+template <int FM, int GM, bool FAST, bool KTAIL, bool OBF16, bool ACC>
+__global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
     int tiles_m, int tiles_n) {
-    constexpr int RB = BK / 2;                     // code bytes per row per stage
-    constexpr int CPR = RB / 16;                   // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;                  // rows per code DMA instruction
-    constexpr int SWZ = 16 / CPR;                  // rows sharing a swizzle value
-    constexpr int SBY = BK / 32;                   // scale bytes per row per stage (one group)
-    constexpr int SW = SBY / 4;                    // scale words per row per stage
-    constexpr int SRPI = 64 / SW;                  // rows per scale DMA instruction
-    constexpr int KS = BK / 64;                    // MFMA k-steps per stage
-    constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
-    constexpr int FM = TM / 32, FN = TN / 32;      // 32x32 MFMA tiles per wave
-    // scale rows are fetched for BM / BN rounded up to whole instructions
-    // over the four waves (the extra rows are never read)
-    constexpr int NW = WM * WN, NT = 64 * NW;      // waves, threads
-    constexpr int BMP = (BM + NW * SRPI - 1) / (NW * SRPI) * (NW * SRPI);
-    constexpr int BNP = (BN + NW * SRPI - 1) / (NW * SRPI) * (NW * SRPI);
-    constexpr int LA = BM / RPI / NW, LB = BN / RPI / NW;        // code DMAs per wave per stage
-    constexpr int SLA = BMP / SRPI / NW, SLB = BNP / SRPI / NW;  // scale DMAs per wave per stage
-    constexpr int DMA_PER_STAGE = LA + LB + (KTAIL ? 0 : SLA + SLB);
-    constexpr int kCodesA = 0, kCodesB = BM * RB;
-    constexpr int kScA = (BM + BN) * RB, kScB = kScA + BMP * SBY;
-    constexpr int kStage = kScB + BNP * SBY;
-    constexpr int D = NBUF - 1;                    // stages of DMA in flight
-    static_assert(BK == 256, "a stage is one 8-block scale group");
-    static_assert(NBUF == 2 || NBUF == 4, "stage ring");
-    static_assert((NW == 4 || NW == 8) && TM % 32 == 0 && TN % 32 == 0, "wave layout");
-    static_assert(BM % (NW * RPI) == 0 && BN % (NW * RPI) == 0, "code DMA split over the waves");
-    static_assert(NBUF * kStage <= 160 * 1024, "LDS");
-    // Stage buffers as distinct arrays: the compiler can then tell that
+    constexpr int BM = 32 * FM, FN = 2;
+    constexpr int kACodes = FM * 4096;                 // FM row groups x 8 chunks of 512 B
+    constexpr int kAScales = 2048;                     // 8 scale DMAs of 32 rows x 8 B
+    constexpr int kSlot = (kACodes + kAScales) > kWaves * kEpiRegion ? (kACodes + kAScales)
+                                                                     : kWaves * kEpiRegion;
+    // VMEM instructions per wave per stage: A codes (FM) and scales (2) by
+    // DMA, B codes (two per k-step) and B scales (two)
+    // (the fast path moves A's scales with one 16-byte DMA per wave)
+    constexpr int kVmStage = FM + (FAST ? 1 : 2) + 2 * kKS + 2;
+    static_assert(FM >= 4 && FM <= 8, "tile rows");
+    static_assert(!(FAST && KTAIL), "the fast path has no contraction tail");
+    constexpr int kWaitStage = 2 * kVmStage - 2;
+    static_assert(kWaitStage <= 63, "vmcnt range");
+    static_assert(kSlots * kSlot <= 160 * 1024, "LDS");
+    // Stage slots as distinct arrays: the compiler can then tell that
     // fragment reads of one do not wait on DMA still landing in another.
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[NBUF > 2 ? kStage : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NBUF > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kSlot];
+    uint8_t* const slots[kSlots] = {lds0, lds1, lds2, lds3};
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int wm = wave / WN, wn = wave % WN, h = lane >> 5, l32 = lane & 31;
-    // Persistent workgroups: tile t, t + gridDim.x, ... (the grid is at most
-    // one workgroup per CU, so consecutive tile indices still land on the
-    // XCDs round-robin).
+    const int h = lane >> 5, l32 = lane & 31;
     const int ntiles = tiles_m * tiles_n;
-    const int64_t kbytes = K / 2, ks = K / 32;
-    const int nk = (int)((K + BK - 1) / BK);
-    // The current tile: origin and buffer views of its rows (rows past M / N
-    // are out of range).  Set before the tile's first DMA, which for all but
-    // a workgroup's first tile may be issued during the previous tile's
-    // epilogue.
+    const int64_t nb = K / 32;                         // blocks per row
+    const int nks = (int)((nb + 1) / 2);               // MFMA k-steps (K < 2^24)
+    const int nk = (int)((nb + 7) / 8);                // 256-k stages
+    // leading all-zero stages round the stage count up to a multiple of the
+    // ring (the loop below handles four stages per iteration)
+    const int kfirst = -((kSlots - nk % kSlots) % kSlots);
+    const uint32_t gstride = (uint32_t)(nb * 512);     // bytes per 32-row group of codes
+
+    // Per-lane parts of the buffer offsets (the stage / k-step part goes in
+    // the scalar offset): A chunk d of this wave's k-step (wave) of a stage,
+    // B fragment j (row group 2 wave + j) of a k-step.
+    uint32_t offa[FM], offb[FN];
+#pragma unroll
+    for (int d = 0; d < FM; ++d) offa[d] = (uint32_t)d * gstride + (uint32_t)lane * 16;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) offb[j] = (uint32_t)(2 * wave + j) * gstride + (uint32_t)lane * 16;
+    // the upper half of a k-step past the last block (nb odd) reads zero
+    const bool half_tail = KTAIL && (nb & 1) && h == 1;
+
     int64_t m0 = 0, n0 = 0, rows_a = 0, rows_b = 0;
     __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0, kBufferWord3);
-    __amdgpu_buffer_rsrc_t rb = ra;
+    __amdgpu_buffer_rsrc_t rb = ra, rsa = ra, rsb = ra;   // rsa, rsb: FAST scale descriptors
+    // FAST: lane parts of the scale offsets (A: 16 bytes of this wave's
+    // 128-row run, B: this lane's row of fragment j)
+    const uint32_t offsa0 = (uint32_t)(((wave & 1) ? (BM - 128) * 8 : 0) + lane * 16);
+    uint32_t offsb[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) offsb[j] = (uint32_t)((64 * wave + 32 * j + l32) * 8);
     auto set_tile = [&](int t) {
         int tile_m, tile_n;
         tile_of_block<GM>(t, ntiles, tiles_m, tiles_n, tile_m, tile_n);
         tile_m = __builtin_amdgcn_readfirstlane(tile_m);
         tile_n = __builtin_amdgcn_readfirstlane(tile_n);
         m0 = (int64_t)tile_m * BM;
-        n0 = (int64_t)tile_n * BN;
+        n0 = (int64_t)tile_n * kBN;
         rows_a = (M - m0) < BM ? (M - m0) : BM;
-        rows_b = (N - n0) < BN ? (N - n0) : BN;
-        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * kbytes), (short)0, (int)(rows_a * kbytes),
-                                               kBufferWord3);
-        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * kbytes), (short)0, (int)(rows_b * kbytes),
-                                               kBufferWord3);
+        rows_b = (N - n0) < kBN ? (N - n0) : kBN;
+        // the tile's row groups of each operand; groups past the operand's
+        // last one are out of range and read as zero
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (m0 / 32) * (int64_t)gstride), (short)0,
+                                               (int)(((rows_a + 31) / 32) * (int64_t)gstride), kBufferWord3);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (n0 / 32) * (int64_t)gstride), (short)0,
+                                               (int)(((rows_b + 31) / 32) * (int64_t)gstride), kBufferWord3);
+        if constexpr (FAST) {
+            // stage q of the tile's rows starts q R 8 bytes further on
+            rsa = __builtin_amdgcn_make_buffer_rsrc((void*)(SA + m0 * 8), (short)0,
+                                                    (int)(((int64_t)nk * M - m0) * 8), kBufferWord3);
+            rsb = __builtin_amdgcn_make_buffer_rsrc((void*)(SB + n0 * 8), (short)0,
+                                                    (int)(((int64_t)nk * N - n0) * 8), kBufferWord3);
+        }
     };
-    // Epilogue staging: with kEarly each wave stages its rows in a quarter of
-    // stage buffer 1 only, so the next tile's first stage can land in stage
-    // buffer 0 meanwhile; otherwise in 32 KB spread over both buffers.
-    constexpr int kRowBytes = TN * 4 + 16;
-    constexpr int kLanesPerRow = TN / 4;
-    constexpr int kRowsPerInst = kLanesPerRow >= 64 ? 1 : 64 / kLanesPerRow;
-    constexpr bool kEarly = !KTAIL && !ACC && NBUF == 2 && 32 * kRowBytes <= kStage / 4 &&
-                            kRowsPerInst * kLanesPerRow == 64;
-    constexpr int kRegion = kEarly ? kStage / 4 / 16 * 16 : 32768;
-    // store instructions of a full tile's epilogue (they follow the next
-    // tile's first DMA in the wave's memory counter)
-    constexpr int kEpiStores = FM * 32 / kRowsPerInst;
-    bool early = false;   // this tile's first stage was issued during the previous epilogue
+
+    // ---- loads ---------------------------------------------------------
+    // A DMA of stage kt into `slot`: chunk d (row group d, k-step `wave` of
+    // the stage) for d in [d0, d1), and the scale runs (two per wave) when
+    // `scales`.  A stage outside [0, nk) is all zero.
+    auto dma_a = [&](int kt, uint8_t* slot, int d0, int d1, bool scales) {
+        if constexpr (FAST) {
+            const int kc = kt < nk ? kt : nk - 1;
+            const int soff = __builtin_amdgcn_readfirstlane((4 * kc + wave) * 1024);
+#pragma unroll
+            for (int d = 0; d < FM; ++d)
+                if (d >= d0 && d < d1) dma16_to_lds(ra, slot + d * 4096 + wave * 1024, offa[d], soff);
+            // the scale run of the stage's BM rows (8 bytes each) by
+            // 16-byte-per-lane DMAs of 128 rows: rows 0..127 (waves 0, 2) and
+            // the last 128 rows of the tile (waves 1, 3; the repeated DMA
+            // writes the same bytes and keeps every wave's instruction count,
+            // hence its waits, identical).  4-byte DMAs cost several times
+            // more per byte on the load path.
+            if (scales) {
+                const int ss = __builtin_amdgcn_readfirstlane((int)((int64_t)kc * M * 8));
+                dma16_to_lds(rsa, slot + kACodes + ((wave & 1) ? (BM - 128) * 8 : 0), offsa0, ss);
+            }
+            return;
+        }
+        const bool zero = kt < 0 || kt >= nk;
+        const int ks = 4 * kt + wave;                  // this wave's k-step
+        bool dead = zero;
+        if constexpr (KTAIL) dead = dead || ks >= nks;
+        const int soff = __builtin_amdgcn_readfirstlane(dead ? 0 : ks * 1024);
+        const uint32_t oob = dead ? kOob : 0u;
+        const uint32_t hoob = (KTAIL && !dead && ks == nks - 1 && half_tail) ? kOob : 0u;
+#pragma unroll
+        for (int d = 0; d < FM; ++d)
+            if (d >= d0 && d < d1)
+                dma16_to_lds(ra, slot + d * 4096 + wave * 1024, offa[d] | oob | hoob, soff);
+        if (scales) {
+            const int64_t q = zero ? 0 : kt;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(SA + (q * M + m0) * 8), (short)0, (int)(rows_a * 8), kBufferWord3);
+            const uint32_t zoob = zero ? kOob : 0u;
+            dma4_to_lds(rs, slot + kACodes + wave * 256, (uint32_t)(wave * 256 + lane * 4) | zoob, 0);
+            dma4_to_lds(rs, slot + kACodes + (wave + 4) * 256,
+                        (uint32_t)((wave + 4) * 256 + lane * 4) | zoob, 0);
+        }
+    };
+    // B fragment j of k-step s (global index) into registers.
+    auto load_b = [&](int s, int j) -> v4i {
+        if constexpr (FAST) {
+            const int soff = __builtin_amdgcn_readfirstlane((s < nks ? s : nks - 1) * 1024);
+            return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, offb[j], soff, 0));
+        }
+        bool dead = s < 0 || s >= nks;
+        const int soff = __builtin_amdgcn_readfirstlane(dead ? 0 : s * 1024);
+        uint32_t off = offb[j] | (dead ? kOob : 0u);
+        if constexpr (KTAIL) off |= (!dead && s == nks - 1 && half_tail) ? kOob : 0u;
+        return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, off, soff, 0));
+    };
+    // B scales of stage kt: this lane's row of fragment j, 8 bytes.
+    struct BSc { uint32_t w[FN][2]; };
+    auto load_bsc = [&](int kt) -> BSc {
+        if constexpr (FAST) {
+            const int kc = kt < nk ? kt : nk - 1;
+            const int ss = __builtin_amdgcn_readfirstlane((int)((int64_t)kc * N * 8));
+            BSc r;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsb, offsb[j], ss, 0);
+                r.w[j][0] = v[0];
+                r.w[j][1] = v[1];
+            }
+            return r;
+        }
+        const bool zero = kt < 0 || kt >= nk;
+        const int64_t q = zero ? 0 : kt;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(SB + (q * N + n0) * 8), (short)0, (int)(rows_b * 8), kBufferWord3);
+        BSc r;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const uint32_t off = (uint32_t)((64 * wave + 32 * j + l32) * 8) | (zero ? kOob : 0u);
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+            r.w[j][0] = v[0];
+            r.w[j][1] = v[1];
+        }
+        return r;
+    };
+
+    // ---- registers -----------------------------------------------------
+    v16f acc[FM][FN];
+    v4i fa[2][FM];                 // A fragments of two k-steps (k-step parity)
+    v4i fb[kRing][FN];             // B fragments, k-step s in fb[s mod 8]
+    BSc bsc[kSlots];               // B scales, stage kt in bsc[(kt - kfirst) mod 4]
+    struct ASc { uint32_t w[FM][2]; };
+    ASc asc[2];                    // A scales of the current and next stage
+
+    auto read_afrags = [&](const uint8_t* slot, int s, int set) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            fa[set][i] = *reinterpret_cast<const v4i*>(slot + i * 4096 + s * 1024 + lane * 16);
+    };
+    auto read_ascales = [&](const uint8_t* slot, int kt, ASc& sc) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const uint2 v = *reinterpret_cast<const uint2*>(slot + kACodes + (i * 32 + l32) * 8);
+            sc.w[i][0] = v.x;
+            sc.w[i][1] = v.y;
+            if constexpr (KTAIL) {
+                sc.w[i][0] = mask_scale_word(sc.w[i][0], (int64_t)kt * 8, nb);
+                sc.w[i][1] = mask_scale_word(sc.w[i][1], (int64_t)kt * 8 + 4, nb);
+            }
+        }
+    };
+    // MFMAs of k-step s (0..3) of a stage: A fragments set, B ring slot r.
+    auto mfmas = [&](int s, int set, int r, const ASc& sa, const BSc& sb, int kt) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const v8i af = __builtin_shufflevector(fa[set][i], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+            const uint32_t wa = sa.w[i][s >> 1] >> (8 * h);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const v8i bf = __builtin_shufflevector(fb[r][j], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+                uint32_t wbw = sb.w[j][s >> 1];
+                if constexpr (KTAIL) wbw = mask_scale_word(wbw, (int64_t)kt * 8 + 4 * (s >> 1), nb);
+                const uint32_t wb = wbw >> (8 * h);
+                acc[i][j] = (s & 1) ? mfma_fp4_byte2(bf, af, acc[i][j], wb, wa)
+                                    : mfma_fp4_byte0(bf, af, acc[i][j], wb, wa);
+            }
+        }
+    };
+
+    // A chunk DMAs of a stage are spread over k-steps 0..2: k-step s issues
+    // chunks [kDma(s), kDma(s + 1)) (the scale runs go with k-step 0).
+    auto kdma = [](int s) { return s * FM / 3 < FM ? s * FM / 3 : FM; };
+
+    // One stage from slot u (its k-step 0 fragments and scales already in
+    // registers).  Stage kt + 3 is loaded into slot (u + 3) mod 4, B scales
+    // of stage kt + 2 into the B scale ring, B k-steps 8 ahead into the B ring.
+    auto run_stage = [&](int u, int kt) {
+        uint8_t* const cur = slots[u];
+        uint8_t* const ahead = slots[(u + 3) % kSlots];
+        uint8_t* const next = slots[(u + 1) % kSlots];
+        const ASc& sa = asc[u & 1];
+        ASc& nsa = asc[(u + 1) & 1];
+        const BSc& sb = bsc[u];
+#pragma unroll
+        for (int s = 0; s < kKS - 1; ++s) {
+            read_afrags(cur, s + 1, (s + 1) & 1);
+            mfmas(s, s & 1, (4 * u + s) % kRing, sa, sb, kt);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[(4 * u + s) % kRing][j] = load_b(4 * kt + s + kRing, j);
+            dma_a(kt + 3, ahead, kdma(s), kdma(s + 1), s == 0);
+            if (s == 0) bsc[(u + 2) % kSlots] = load_bsc(kt + 2);
+            // interleave: one MFMA, then a DS read and a VMEM op spread evenly
+            constexpr int kM = FM * FN;
+            const int nvm = FN + (kdma(s + 1) - kdma(s)) + (s == 0 ? (FAST ? 1 : 2) + FN : 0);
+#pragma unroll
+            for (int t = 0; t < kM; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+                if ((t + 1) * FM / kM > t * FM / kM)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+                if ((t + 1) * nvm / kM > t * nvm / kM)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // this wave's DMA of stage kt + 1 (issued two stages ago) has landed,
+        // and its fragment reads of `cur` are done; the barrier publishes
+        // every wave's part of stage kt + 1.  At least 2 kVmStage - 2 VMEM
+        // instructions follow the last one of stage kt + 1: all of stage
+        // kt - 1, stage kt up to here, the B loads closing stage kt - 2 (the
+        // prologue's order gives exactly that count for the first stages).
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kWaitStage));
+        barrier_after_wait();
+        read_ascales(next, kt + 1, nsa);
+        read_afrags(next, 0, 0);
+        mfmas(kKS - 1, 1, (4 * u + 3) % kRing, sa, sb, kt);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[(4 * u + 3) % kRing][j] = load_b(4 * kt + 3 + kRing, j);
+        constexpr int kM = FM * FN, kDs = 2 * FM;
+#pragma unroll
+        for (int t = 0; t < kM; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+            if ((t + 1) * kDs / kM > t * kDs / kM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if ((t + 1) * kDs / kM > t * kDs / kM + 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if ((t + 1) * FN / kM > t * FN / kM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // The first stages of a tile: A stages kfirst .. kfirst+2 into slots
+    // 0..2, B scales of the first two stages, B k-steps of the first two
+    // stages.  Issued in stage order so that the wait for stage kfirst
+    // counts everything after its A part.
+    // (The scheduling barriers keep this order: the waits the compiler puts
+    // before the first MFMAs of every loop iteration are the deeper of the
+    // loop's own distance and this prologue's.)
+    auto prologue = [&]() {
+        dma_a(kfirst, slots[0], 0, FM, true);
+        __builtin_amdgcn_sched_barrier(0);
+        bsc[0] = load_bsc(kfirst);
+#pragma unroll
+        for (int s = 0; s < kKS; ++s)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[s][j] = load_b(4 * kfirst + s, j);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_a(kfirst + 1, slots[1], 0, FM, true);
+        __builtin_amdgcn_sched_barrier(0);
+        bsc[1] = load_bsc(kfirst + 1);
+#pragma unroll
+        for (int s = kKS; s < 2 * kKS; ++s)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[s][j] = load_b(4 * kfirst + s, j);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_a(kfirst + 2, slots[2], 0, FM, true);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // VMEM issued after stage kfirst's A part in the prologue: its B scales,
+    // the B loads of two stages, two more A stages and one more B scale load
+    constexpr int kPro = FN + 2 * kKS * FN + 2 * (FM + (FAST ? 1 : 2)) + FN;
+    // stores of a full tile's epilogue per wave (32-row pieces, 4 rows per
+    // store instruction)
+    constexpr int kEpiStores = FM * 8;
+
+    bool early = false;   // this tile's prologue was issued during the previous epilogue
     for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
         if (!early) {
-            // every wave is done with the previous tile's LDS before it is refilled
             if (t != (int)blockIdx.x) {
+                // every wave is done with the previous tile's LDS before it is refilled
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
                 barrier_after_wait();
             }
             set_tile(t);
-        }
-
-        // Per-lane DMA offsets within the stage at k = 0; the stage's k offset
-        // goes in the scalar offset.  Codes: row lane / CPR of an RPI-row group,
-        // the chunk that belongs in slot lane mod CPR of that row.  Scales: the
-        // contiguous groups of an SRPI-row run, one word per lane.
-        const int drow = lane / CPR, dslot = lane % CPR;
-        uint32_t offa[LA], offb[LB], offsa[SLA], offsb[SLB];
-        int chka[LA], chkb[LB];   // byte offset of the fetched chunk within the row
-    #pragma unroll
-        for (int i = 0; i < LA; ++i) {
-            const int row = (wave * LA + i) * RPI + drow;
-            chka[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
-            offa[i] = (uint32_t)(row * kbytes + chka[i]);
-        }
-    #pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            const int row = (wave * LB + i) * RPI + drow;
-            chkb[i] = (dslot ^ ((row / SWZ) % CPR)) * 16;
-            offb[i] = (uint32_t)(row * kbytes + chkb[i]);
-        }
-    #pragma unroll
-        for (int i = 0; i < SLA; ++i)
-            offsa[i] = (uint32_t)(((wave * SLA + i) * SRPI * SBY) + lane * 4);
-    #pragma unroll
-        for (int i = 0; i < SLB; ++i)
-            offsb[i] = (uint32_t)(((wave * SLB + i) * SRPI * SBY) + lane * 4);
-
-        // A stage kt outside [0, nk) is an all-zero stage (every offset out of
-        // range, zero codes and scale bytes).  Leading zero stages round the
-        // stage count up to a multiple of NBUF for the loop below; trailing ones
-        // are the (unused) prefetches past the last stage, which keep every
-        // stage one straight-line block.
-        auto load_stage = [&](int kt, uint8_t* base) {
-            const bool zero = kt < 0 || kt >= nk;
-            const int kcode = __builtin_amdgcn_readfirstlane(zero ? 0 : kt * RB);
-            // a chunk past the contraction end gets an offset out of range
-            const uint32_t oob = zero ? 0x80000000u : 0u;
-    #pragma unroll
-            for (int i = 0; i < LA; ++i) {
-                const uint32_t tail = KTAIL ? (uint32_t)(kcode + chka[i] >= kbytes) << 31 : 0u;
-                dma16_to_lds(ra, base + kCodesA + (wave * LA + i) * RPI * RB, offa[i] | oob | tail, kcode);
-            }
-    #pragma unroll
-            for (int i = 0; i < LB; ++i) {
-                const uint32_t tail = KTAIL ? (uint32_t)(kcode + chkb[i] >= kbytes) << 31 : 0u;
-                dma16_to_lds(rb, base + kCodesB + (wave * LB + i) * RPI * RB, offb[i] | oob | tail, kcode);
-            }
-            if constexpr (!KTAIL) {
-                // group kt of this tile's rows: one contiguous run per operand
-                const int64_t g = zero ? 0 : kt;
-                const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(SA + (g * M + m0) * SBY), (short)0, (int)(rows_a * SBY), kBufferWord3);
-                const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(SB + (g * N + n0) * SBY), (short)0, (int)(rows_b * SBY), kBufferWord3);
-    #pragma unroll
-                for (int i = 0; i < SLA; ++i)
-                    dma4_to_lds(rsa, base + kScA + (wave * SLA + i) * SRPI * SBY, offsa[i] | oob, 0);
-    #pragma unroll
-                for (int i = 0; i < SLB; ++i)
-                    dma4_to_lds(rsb, base + kScB + (wave * SLB + i) * SRPI * SBY, offsb[i] | oob, 0);
-            } else {
-                for (int r = tid; r < BM; r += NT) {
-                    const int64_t g = m0 + r < M ? m0 + r : M - 1;
-    #pragma unroll
-                    for (int w = 0; w < SW; ++w)
-                        reinterpret_cast<uint32_t*>(base + kScA + r * SBY)[w] =
-                            zero ? 0u : scale_word_masked(SA, M, g, ks, kt, w);
-                }
-                for (int r = tid; r < BN; r += NT) {
-                    const int64_t g = n0 + r < N ? n0 + r : N - 1;
-    #pragma unroll
-                    for (int w = 0; w < SW; ++w)
-                        reinterpret_cast<uint32_t*>(base + kScB + r * SBY)[w] =
-                            zero ? 0u : scale_word_masked(SB, N, g, ks, kt, w);
-                }
-            }
-        };
-
-        v16f acc[FM][FN];
-    #pragma unroll
-        for (int i = 0; i < FM; ++i)
-    #pragma unroll
-            for (int j = 0; j < FN; ++j)
-    #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        // Register state: the fragments of two k-steps (k-step s in set s mod 2)
-        // and the scale words of two stages (word w of a fragment row holds the
-        // blocks of k-steps 2w and 2w+1).  Shifted right by 8 h, word s / 2 holds
-        // this lane's block of k-step s in byte 0 (even s) or byte 2 (odd s),
-        // which the MFMA selects by op_sel.
-        struct Scales { uint32_t a[FM][SW], b[FN][SW]; };
-        // native vectors (not HIP's uint4 struct): one 16-byte LDS load each
-        v4i fa[2][FM], fb[2][FN];
-        auto read_frags = [&](const uint8_t* base, int s) {
-            const uint8_t* la = base + kCodesA + wm * TM * RB;
-            const uint8_t* lb = base + kCodesB + wn * TN * RB;
-    #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = i * 32 + l32;
-                fa[s & 1][i] = *reinterpret_cast<const v4i*>(
-                    la + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
-            }
-    #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = j * 32 + l32;
-                fb[s & 1][j] = *reinterpret_cast<const v4i*>(
-                    lb + row * RB + (((2 * s + h) ^ ((row / SWZ) % CPR)) << 4));
-            }
-        };
-        auto read_scales = [&](const uint8_t* base, Scales& sc) {
-    #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const uint8_t* p = base + kScA + (wm * TM + i * 32 + l32) * SBY;
-    #pragma unroll
-                for (int w = 0; w < SW; ++w) sc.a[i][w] = reinterpret_cast<const uint32_t*>(p)[w];
-            }
-    #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const uint8_t* p = base + kScB + (wn * TN + j * 32 + l32) * SBY;
-    #pragma unroll
-                for (int w = 0; w < SW; ++w) sc.b[j][w] = reinterpret_cast<const uint32_t*>(p)[w];
-            }
-        };
-        auto mfmas = [&](int s, const Scales& sc) {
-    #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const v8i af = __builtin_shufflevector(fa[s & 1][i], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-                const uint32_t wa = sc.a[i][s >> 1] >> (8 * h);
-    #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const v8i bf = __builtin_shufflevector(fb[s & 1][j], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-                    const uint32_t wb = sc.b[j][s >> 1] >> (8 * h);
-                    acc[i][j] = (s & 1) ? mfma_fp4_byte2(bf, af, acc[i][j], wb, wa)
-                                        : mfma_fp4_byte0(bf, af, acc[i][j], wb, wa);
-                }
-            }
-        };
-
-        // One stage from buffer `cur` (its k-step 0 fragments and scales already
-        // in registers as `sc`); `ahead` receives stage kt + D, `next` holds
-        // stage kt + 1.
-        auto run_stage = [&](const uint8_t* cur, int kt, uint8_t* ahead, const uint8_t* next,
-                             const Scales& sc, Scales& nsc) {
-            load_stage(kt + D, ahead);
-    #pragma unroll
-            for (int s = 0; s < KS - 1; ++s) {
-                read_frags(cur, s + 1);
-                mfmas(s, sc);
-            }
-            constexpr int kMfma1 = (KS - 1) * FM * FN, kDs1 = (KS - 1) * (FM + FN);
-            int dma_left = DMA_PER_STAGE;
-    #pragma unroll
-            for (int t = 0; t < kMfma1; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-                if (dma_left > 0) {
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
-                    --dma_left;
-                }
-                // fragment reads spread evenly over the MFMAs
-                if ((t + 1) * kDs1 / kMfma1 > t * kDs1 / kMfma1)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // this wave's DMA of stage kt + 1 has landed (only the D - 1 younger
-            // stages may still be in flight) and its reads of `cur` are done
-            if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-            else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
-            barrier_after_wait();
-            read_scales(next, nsc);
-            read_frags(next, 0);
-            mfmas(KS - 1, sc);
-            constexpr int kMfma2 = FM * FN, kDs2 = (FM + FN) * (1 + SW);
-    #pragma unroll
-            for (int t = 0; t < kMfma2; ++t) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-                if ((t + 1) * kDs2 / kMfma2 > t * kDs2 / kMfma2)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                if ((t + 1) * kDs2 / kMfma2 > t * kDs2 / kMfma2 + 1)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        };
-
-        uint8_t* const bufs[4] = {lds0, lds1, lds2, lds3};
-        const int kfirst = -((NBUF - nk % NBUF) % NBUF);
-        if (!early) {
-    #pragma unroll
-            for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
-            if constexpr (KTAIL) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-            else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((D - 1) * DMA_PER_STAGE));
+            prologue();
+            // (a full drain, once per tile issued this way: the compiler's
+            // own waits before the first MFMAs of each loop iteration then
+            // follow the loop's steady state, not this prologue's order)
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
         } else {
-            // the first stage went out before the previous tile's kEpiStores
-            // stores (the memory counter completes in order)
-            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kEpiStores < 63 ? kEpiStores : 63));
+            // the prologue went out before the previous tile's kEpiStores stores
+            // (the memory counter completes in order)
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kPro + kEpiStores < 63 ? kPro + kEpiStores : 63));
         }
         barrier_after_wait();
-        Scales sc0, sc1;
-        read_scales(bufs[0], sc0);
-        read_frags(bufs[0], 0);
-        for (int kt = kfirst; kt < nk; kt += NBUF) {
-    #pragma unroll
-            for (int b = 0; b < NBUF; ++b) {
-                if (b & 1)
-                    run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc1, sc0);
-                else
-                    run_stage(bufs[b], kt + b, bufs[(b + D) % NBUF], bufs[(b + 1) % NBUF], sc0, sc1);
-            }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        read_ascales(slots[0], kfirst, asc[0]);
+        read_afrags(slots[0], 0, 0);
+        for (int kt = kfirst; kt < nk; kt += kSlots) {
+            run_stage(0, kt);
+            run_stage(1, kt + 1);
+            run_stage(2, kt + 2);
+            run_stage(3, kt + 3);
         }
 
-        // the prefetches past the last stage must land before the workgroup
-        // (and its LDS) goes away
+        // the prefetches past the last stage must land before the slots are
+        // refilled (and before the workgroup goes away)
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
         __syncthreads();                                // all fragment reads of the tile are done
         const int64_t em0 = m0, en0 = n0;               // the tile the epilogue writes
         const bool vec_store = (N % 4) == 0;
-        const bool full_tile = vec_store && em0 + BM <= M && en0 + BN <= N;   // workgroup-uniform
+        const bool full_tile = vec_store && em0 + BM <= M && en0 + kBN <= N;   // workgroup-uniform
         early = false;
-        if constexpr (kEarly) {
-            // The next tile's first stage goes out now, into stage buffer 0
-            // (this epilogue stages in buffer 1 only); it is waited for at
-            // the start of the next tile.
+        if constexpr (!KTAIL && !ACC) {
+            // The next tile's first stages go out now, into slots 0..2 (this
+            // epilogue stages in slot 3); waited for at the next tile's start.
             const int tn = t + (int)gridDim.x;
             if (full_tile && tn < ntiles) {
                 set_tile(tn);
-    #pragma unroll
-                for (int d = 0; d < D; ++d) load_stage(kfirst + d, bufs[d]);
+                prologue();
                 early = true;
             }
         }
 
         // acc[i][j] holds C^T of a 32x32 tile: register r of lane l is
-        // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.  The wave's rows
-        // go out through LDS: the stage buffers are free once every wave is
-        // past its last fragment read; each wave stages a few 32-row pieces of
-        // its tile at a time in its own region (rows padded by 16 bytes:
-        // conflict-free writes of the accumulator layout and row reads), then
-        // reads back four consecutive n of a row per lane, TN / 4 lanes per
-        // row, so that a store instruction covers whole rows of the tile.
-        // fp32 rows are whole 128-byte lines, written non-temporally; with
-        // N % 4 != 0 (rows not 16-byte aligned) elements go one by one.
-        static_assert(NW == 4 && kStage >= 65536 && 32 * kRowBytes <= kRegion && kLanesPerRow <= 64,
-                      "each wave stages at least 32 rows of its tile");
-        constexpr int ICH = (kRegion / kRowBytes) / 32 < FM ? (kRegion / kRowBytes) / 32 : FM;
-        uint8_t* const reg = kEarly ? lds1 + wave * kRegion : ((wave >> 1) ? lds1 : lds0) + (wave & 1) * 32768;
-    #pragma unroll
-        for (int i0 = 0; i0 < FM; i0 += ICH) {
-    #pragma unroll
-            for (int ii = 0; ii < ICH; ++ii) {
-                if (i0 + ii >= FM) break;
-    #pragma unroll
-                for (int j = 0; j < FN; ++j)
-    #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int row = ii * 32 + l32, cn = j * 32 + 8 * q + 4 * h;
-                        *reinterpret_cast<float4*>(reg + row * kRowBytes + cn * 4) =
-                            make_float4(acc[i0 + ii][j][4 * q], acc[i0 + ii][j][4 * q + 1],
-                                        acc[i0 + ii][j][4 * q + 2], acc[i0 + ii][j][4 * q + 3]);
-                    }
-            }
-            const int nrows = (FM - i0 < ICH ? FM - i0 : ICH) * 32;
-            const int lr = lane / kLanesPerRow, c4 = (lane % kLanesPerRow) * 4;
-            const bool lane_on = lr < kRowsPerInst;
+        // n = 8 (r / 4) + 4 (l / 32) + r mod 4, m = l mod 32.  Each wave
+        // stages 32 rows x its 64 columns at a time in its quarter of slot 3
+        // (rows padded by 16 bytes: conflict-free writes of the accumulator
+        // layout and row reads), then reads back four consecutive n of a row
+        // per lane, 16 lanes per row, so that one store instruction writes
+        // four whole rows of the wave's columns (fp32: two 128-byte lines
+        // each, written non-temporally); with N % 4 != 0 (rows not 16-byte
+        // aligned) elements go one by one.
+        uint8_t* const reg = lds3 + wave * kEpiRegion;
+        const int lr = lane >> 4, c4 = (lane & 15) * 4;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int cn = j * 32 + 8 * q + 4 * h;
+                    *reinterpret_cast<float4*>(reg + l32 * kEpiRow + cn * 4) =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]);
+                }
             if (full_tile) {
-                // every row and column in range: batches of kBatch row
-                // reads go out back to back, then their stores
-                constexpr int kBatch = 8;
-    #pragma unroll
-                for (int rb = 0; rb < ICH * 32; rb += kBatch * kRowsPerInst) {
-                    if (rb >= nrows) break;
-                    float4 f[kBatch];
-    #pragma unroll
-                    for (int k = 0; k < kBatch; ++k)
-                        f[k] = *reinterpret_cast<const float4*>(
-                            reg + (lane_on ? rb + k * kRowsPerInst + lr : 0) * kRowBytes + c4 * 4);
-                    if (lane_on) {
-    #pragma unroll
-                        for (int k = 0; k < kBatch; ++k) {
-                            const int64_t m = em0 + wm * TM + i0 * 32 + rb + k * kRowsPerInst + lr;
-                            const int64_t n = en0 + wn * TN + c4;
-                            float v[4] = {f[k].x, f[k].y, f[k].z, f[k].w};
-                            if constexpr (OBF16) {
-                                uint2* p = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + m * N + n);
-                                if constexpr (ACC) {
-                                    const uint2 o = *p;
-                                    v[0] += bf16_value(o.x & 0xFFFFu); v[1] += bf16_value(o.x >> 16);
-                                    v[2] += bf16_value(o.y & 0xFFFFu); v[3] += bf16_value(o.y >> 16);
-                                }
-                                *p = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                                                bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
-                            } else {
-                                float* p = reinterpret_cast<float*>(C) + m * N + n;
-                                if constexpr (ACC) {
-                                    const float4 o = *reinterpret_cast<const float4*>(p);
-                                    v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
-                                }
-                                store_c_line_part(p, make_float4(v[0], v[1], v[2], v[3]));
-                            }
+                float4 f[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    f[k] = *reinterpret_cast<const float4*>(reg + (4 * k + lr) * kEpiRow + c4 * 4);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int64_t m = em0 + i * 32 + 4 * k + lr;
+                    const int64_t n = en0 + 64 * wave + c4;
+                    float v[4] = {f[k].x, f[k].y, f[k].z, f[k].w};
+                    if constexpr (OBF16) {
+                        uint2* p = reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(C) + m * N + n);
+                        if constexpr (ACC) {
+                            const uint2 o = *p;
+                            v[0] += bf16_value(o.x & 0xFFFFu); v[1] += bf16_value(o.x >> 16);
+                            v[2] += bf16_value(o.y & 0xFFFFu); v[3] += bf16_value(o.y >> 16);
                         }
+                        *p = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                        bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+                    } else {
+                        float* p = reinterpret_cast<float*>(C) + m * N + n;
+                        if constexpr (ACC) {
+                            const float4 o = *reinterpret_cast<const float4*>(p);
+                            v[0] += o.x; v[1] += o.y; v[2] += o.z; v[3] += o.w;
+                        }
+                        store_c_line_part(p, make_float4(v[0], v[1], v[2], v[3]));
                     }
                 }
                 continue;
             }
-    #pragma unroll
-            for (int rr = 0; rr < ICH * 32; rr += kRowsPerInst) {
-                if (rr >= nrows) break;
-                const int row = rr + lr;
-                const float4 f = *reinterpret_cast<const float4*>(reg + (lane_on ? row : 0) * kRowBytes + c4 * 4);
-                const int64_t m = em0 + wm * TM + i0 * 32 + row, n = en0 + wn * TN + c4;
-                if (!lane_on || m >= M) continue;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int row = 4 * k + lr;
+                const float4 f = *reinterpret_cast<const float4*>(reg + row * kEpiRow + c4 * 4);
+                const int64_t m = em0 + i * 32 + row, n = en0 + 64 * wave + c4;
+                if (m >= M || n >= N) continue;
                 float v[4] = {f.x, f.y, f.z, f.w};
                 if constexpr (OBF16) {
                     uint16_t* crow = reinterpret_cast<uint16_t*>(C) + m * N;
@@ -588,48 +610,60 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_tn(
     }
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of each device, queried once per device (concurrent first
+// calls may both query; they store the same value).
 int cu_count() {
-    static int counts[64] = {0};
+    static std::atomic<int> counts[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (counts[dev] == 0) {
-        int n = 0;
+    int n = counts[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        counts[dev] = n;
+        counts[dev].store(n, std::memory_order_relaxed);
     }
-    return counts[dev];
+    return n;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM, bool OBF16, bool ACC>
-void launch_kernel(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
-                   int64_t M, int64_t N, int64_t K, void* c, hipStream_t st) {
-    const int64_t tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    const int64_t grid = tm * tn < cu_count() ? tm * tn : cu_count();
-    if (K % BK == 0) {
-        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, false, OBF16, ACC>),
-                           dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K,
-                           c, (int)tm, (int)tn);
-    } else {
-        hipLaunchKernelGGL((gemm_mx_tn<BM, BN, WM, WN, BK, NBUF, GM, true, OBF16, ACC>),
-                           dim3((unsigned)grid), dim3(64 * WM * WN), 0, st, aq, as, bq, bs, M, N, K,
-                           c, (int)tm, (int)tn);
-    }
+// Tile-rows per group of the block order (each XCD runs 32 tiles at a time):
+// groups of 2 to 4 rows measured best on the gate/up and q_proj shapes.
+constexpr int kGroupRows = 4;
+
+template <int FM, bool FAST, bool KTAIL, bool OBF16, bool ACC>
+hipError_t launch_one(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                      int64_t M, int64_t N, int64_t K, void* c, dim3 grid, int tm, int tn, hipStream_t st) {
+    void (*k)(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, int64_t, int64_t, int64_t,
+              void*, int, int) = gemm_mx_tn<FM, kGroupRows, FAST, KTAIL, OBF16, ACC>;
+    void* args[] = {(void*)&aq, (void*)&as, (void*)&bq, (void*)&bs, (void*)&M, (void*)&N,
+                    (void*)&K, (void*)&c, (void*)&tm, (void*)&tn};
+    return hipLaunchKernel((const void*)k, grid, dim3(kThreads), args, 0, st);
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NBUF, int GM>
-hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
-                        const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* c, int out_bf16,
-                        int accumulate, hipStream_t st) {
-    if (out_bf16) {
-        if (accumulate) launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, true, true>(aq, as, bq, bs, M, N, K, c, st);
-        else launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, true, false>(aq, as, bq, bs, M, N, K, c, st);
-    } else {
-        if (accumulate) launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, false, true>(aq, as, bq, bs, M, N, K, c, st);
-        else launch_kernel<BM, BN, WM, WN, BK, NBUF, GM, false, false>(aq, as, bq, bs, M, N, K, c, st);
-    }
-    return hipGetLastError();
+template <int FM, bool OBF16, bool ACC>
+hipError_t launch_kernel(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                         int64_t M, int64_t N, int64_t K, void* c, hipStream_t st) {
+    const int64_t tm = (M + 32 * FM - 1) / (32 * FM), tn = (N + kBN - 1) / kBN;
+    const int64_t cus = cu_count();
+    const dim3 grid((unsigned)(tm * tn < cus ? tm * tn : cus));
+    // the fast path: full tiles, K a multiple of 1024, and every scale
+    // offset (stage q of row r at (q R + r) 8) within 31 bits
+    const bool fast = M % (32 * FM) == 0 && N % kBN == 0 && K % 1024 == 0 &&
+                      (K / 256) * (M > N ? M : N) * 8 < (INT64_C(1) << 31);
+    if (fast) return launch_one<FM, true, false, OBF16, ACC>(aq, as, bq, bs, M, N, K, c, grid, (int)tm, (int)tn, st);
+    if (K % 256 == 0)
+        return launch_one<FM, false, false, OBF16, ACC>(aq, as, bq, bs, M, N, K, c, grid, (int)tm, (int)tn, st);
+    return launch_one<FM, false, true, OBF16, ACC>(aq, as, bq, bs, M, N, K, c, grid, (int)tm, (int)tn, st);
+}
+
+template <int FM>
+hipError_t launch_out(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs,
+                      int64_t M, int64_t N, int64_t K, void* c, int out_bf16, int accumulate,
+                      hipStream_t st) {
+    if (out_bf16)
+        return accumulate ? launch_kernel<FM, true, true>(aq, as, bq, bs, M, N, K, c, st)
+                          : launch_kernel<FM, true, false>(aq, as, bq, bs, M, N, K, c, st);
+    return accumulate ? launch_kernel<FM, false, true>(aq, as, bq, bs, M, N, K, c, st)
+                      : launch_kernel<FM, false, false>(aq, as, bq, bs, M, N, K, c, st);
 }
 
 }  // namespace
@@ -637,25 +671,18 @@ hipError_t launch_tiles(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
 hipError_t launch_gemm_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
                           const uint8_t* bs, int64_t M, int64_t N, int64_t K, void* c,
                           int out_bf16, int accumulate, hipStream_t st) {
-    // Tile shape: the persistent grid runs ceil(tiles / CUs) rounds of one
-    // tile per CU, each costing about the tile's area, so pick the shape with
-    // the least rounds x area (256 x 256 unless a 224-row or -column tile
-    // removes a partly idle last round, e.g. M = 14336 = 64 x 224).
+    // Tile rows: the persistent grid runs ceil(tiles / CUs) rounds of one
+    // tile per CU, each costing about the tile's area, so take the height
+    // with the least rounds x height (256 unless 224 removes a partly idle
+    // last round, e.g. M = 14336 = 64 x 224).
     const int64_t cus = cu_count();
-    // Tile-rows per group of the block order.  Measured on the gate/up and
-    // q_proj shapes (each XCD runs 32 tiles at a time): groups of 2 to 4
-    // rows beat 8 by 2-5 % and 16 by more; 4 is the best on average.
-    constexpr int kGroupRows = 4;
-    auto cost = [&](int64_t bm, int64_t bn) {
-        const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-        return ((tiles + cus - 1) / cus) * bm * bn;
+    const int64_t tn = (N + kBN - 1) / kBN;
+    auto cost = [&](int64_t bm) {
+        const int64_t tiles = ((M + bm - 1) / bm) * tn;
+        return ((tiles + cus - 1) / cus) * bm;
     };
-    const int64_t c256 = cost(256, 256), cm = cost(224, 256), cn = cost(256, 224);
-    if (cm < c256 && cm <= cn)
-        return launch_tiles<224, 256, 1, 4, 256, 2, kGroupRows>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
-    if (cn < c256)
-        return launch_tiles<256, 224, 4, 1, 256, 2, kGroupRows>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
-    return launch_tiles<256, 256, 2, 2, 256, 2, kGroupRows>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
+    if (cost(224) < cost(256)) return launch_out<7>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
+    return launch_out<8>(aq, as, bq, bs, M, N, K, c, out_bf16, accumulate, st);
 }
 
 }  // namespace fp4dev

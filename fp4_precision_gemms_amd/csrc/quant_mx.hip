@@ -7,17 +7,23 @@
 // нестабильности": a Hadamard transform, deterministic or after random sign
 // flips, applied before quantization.
 //
-// Scales are written k-grouped, the layout the GEMM stages load in one
-// contiguous run: for an output of R rows (the logical rows of x or x^T) and
-// nb blocks per row, block b of row r goes to byte ((b / 8) R + r) * 8 +
-// b mod 8.  Bytes of the last group past nb are not written.
+// Output layouts (those the GEMM loads), for an output of R rows (the
+// logical rows of x or x^T) and nb blocks per row:
+//   - codes, 32-row tiled: the 16 code bytes of block b of row r at
+//     ((r / 32) nb + b) * 512 + 16 (r mod 32), i.e. for each group of 32
+//     rows and each block one contiguous 512-byte chunk.  Rows of the last
+//     group past R are not written.
+//   - scales, k-grouped: block b of row r at byte ((b / 8) R + r) * 8 +
+//     b mod 8.  Bytes of the last group past nb are not written.
 //
 // Kernels, by block axis:
-//   quant_mx_along_cols -- blocks run along the contiguous dim.  A lane owns 8
-//     consecutive elements (one 16-byte load); four adjacent lanes own a
-//     block.  The first three butterfly stages are in registers, the strides
-//     8 and 16 cross lanes through DPP quad permutes, the block maximum is a
-//     two-step DPP reduction, and each lane stores its 8 codes as one dword.
+//   quant_mx_along_cols -- blocks run along the contiguous dim.  A workgroup
+//     owns 32 rows x 256 columns; a lane owns 8 consecutive elements (one
+//     16-byte load); four adjacent lanes own a block.  The first three
+//     butterfly stages are in registers, the strides 8 and 16 cross lanes
+//     through DPP quad permutes, the block maximum is a two-step DPP
+//     reduction, and each lane stores its 8 codes as one dword: the
+//     workgroup writes 8 whole 512-byte chunks.
 //   quant_mx_along_rows_lds -- blocks run along the strided dim (x^T is
 //     quantized, as Wgrad needs: blocks along tokens).  32 x 256 bf16 tiles
 //     go global -> LDS by DMA, one thread per column transposes through LDS,
@@ -111,26 +117,45 @@ __device__ __forceinline__ uint32_t encode8_sw(const float* y, uint32_t byte, ui
 constexpr int kColsThreads = 256;
 constexpr int kColsUnroll = 4;
 
+// Byte offset of the 16 code bytes of (row r, block b) in the 32-row tiled
+// layout of an operand with nb blocks per row: chunk (r / 32, b) of 512
+// bytes, row r mod 32 at 16 (r mod 32).
+__device__ __forceinline__ int64_t tiled_offset(int64_t r, int64_t b, int64_t nb) {
+    return ((r >> 5) * nb + b) * 512 + (r & 31) * 16;
+}
+
+// Blocks along cols.  A workgroup owns 32 rows x 256 columns (8 blocks per
+// row): chunk i = u * 256 + tid of its kColsUnroll x 256 16-byte loads is
+// row i / 32, 8-column chunk i mod 32, so each wave load instruction reads
+// two 512-byte row segments and a lane quad holds one 32-element block.
+// The workgroup's codes are 8 whole chunks of the tiled layout (4 KB).
 // HADN: 0 (no rotation), 16 or 32.
 template <int HADN, bool SR>
 __global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
-    const uint4* __restrict__ x, int64_t nchunks, uint32_t sign_word, float norm,
-    uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t nb,
-    int64_t nrows, double inv_nb) {
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
+    uint64_t sr_seed, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int64_t nb = cols / 32;
+    const int64_t gx = (cols + 255) / 256;           // workgroups per row group (1-D grid)
+    const int64_t c0 = ((int64_t)blockIdx.x % gx) * 256, r0 = ((int64_t)blockIdx.x / gx) * 32;
+    const int tid = threadIdx.x;
+    const int q = tid & 3;                         // lane within the block of 4
     uint4 w[kColsUnroll];
-    int64_t g[kColsUnroll];
+    int64_t row[kColsUnroll], col[kColsUnroll];
+    bool in[kColsUnroll];
 #pragma unroll
     for (int u = 0; u < kColsUnroll; ++u) {
-        g[u] = ((int64_t)blockIdx.x * kColsUnroll + u) * kColsThreads + threadIdx.x;
-        if (g[u] < nchunks) w[u] = x[g[u]];
+        const int i = u * kColsThreads + tid;
+        row[u] = r0 + (i >> 5);
+        col[u] = c0 + (i & 31) * 8;
+        in[u] = row[u] < rows && col[u] < cols;    // uniform per quad: cols % 32 == 0
+        if (in[u]) w[u] = *reinterpret_cast<const uint4*>(x + row[u] * cols + col[u]);
     }
-    const int q = threadIdx.x & 3;                 // lane within the block of 4
     // sign-bit masks of the cross-lane butterfly stages: the upper lane of a
     // pair computes partner - own as partner + (-own)
     const uint32_t neg1 = (uint32_t)(q & 1) << 31, neg2 = (uint32_t)((q >> 1) & 1) << 31;
 #pragma unroll
     for (int u = 0; u < kColsUnroll; ++u) {
-        if (g[u] >= nchunks) break;                // uniform per quad: nchunks % 4 == 0
+        if (!in[u]) continue;
         float a[8] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y),
                       bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
         if constexpr (HADN != 0) {
@@ -165,23 +190,17 @@ __global__ __launch_bounds__(kColsThreads) void quant_mx_along_cols(
             } else {
                 uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
                 if constexpr (SR) {
-                    u0 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2);
-                    u1 = stream4(sr_seed, 0u, (uint64_t)g[u] * 2 + 1);
+                    // elements idx .. idx+7 (idx = row * cols + col): counters idx/4, idx/4 + 1
+                    const uint64_t g = ((uint64_t)row[u] * (uint64_t)cols + (uint64_t)col[u]) >> 2;
+                    u0 = stream4(sr_seed, 0u, g);
+                    u1 = stream4(sr_seed, 0u, g + 1);
                 }
                 word = encode8_sw<SR>(a, byte, u0, u1);
             }
         }
-        codes[g[u]] = word;
-        if (q == 0) {
-            // block (r, b) of the flat block index; the double quotient is
-            // off by at most one for any index below 2^52
-            const int64_t blk = g[u] >> 2;
-            int64_t r = (int64_t)((double)blk * inv_nb);
-            if (r * nb > blk) --r;
-            if ((r + 1) * nb <= blk) ++r;
-            const int64_t b = blk - r * nb;
-            scales[((b >> 3) * nrows + r) * 8 + (b & 7)] = (uint8_t)byte;
-        }
+        const int64_t b = col[u] >> 5;
+        *reinterpret_cast<uint32_t*>(codes + tiled_offset(row[u], b, nb) + 4 * q) = word;
+        if (q == 0) scales[((b >> 3) * rows + row[u]) * 8 + (b & 7)] = (uint8_t)byte;
     }
 }
 
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
                 }
                 out = make_uint4(wd[0], wd[1], wd[2], wd[3]);
             }
-            *reinterpret_cast<uint4*>(codes + col * (rows / 2) + rb * 16) = out;
+            *reinterpret_cast<uint4*>(codes + tiled_offset(col, rb, nrb)) = out;
             sword[c] |= byte << (8 * i);
         }
     }
@@ -400,7 +419,7 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
     uint64_t sr_seed_in, uint8_t* __restrict__ codes_in, uint8_t* __restrict__ scales_in,
     uint32_t sign_word_c, float norm_c, uint64_t sr_seed_c, uint8_t* __restrict__ codes_c,
     uint8_t* __restrict__ scales_c, RowsLdsSecond second) {
-    static_assert(TB == 2 || TB == 4 || TB == 8, "blocks per workgroup");
+    static_assert(TB == 2, "two blocks per workgroup: one 64-element k-step of the tiled codes");
     constexpr int kTileBlocks = TB;
     __shared__ __attribute__((aligned(1024))) uint16_t tile[kTileBlocks][32 * kTileCols];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -493,7 +512,7 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
                 uint32_t wc[4];
                 const uint64_t gb = ((uint64_t)row * (uint64_t)cols + (uint64_t)cb) >> 2;
                 const uint32_t bc = quant_block32<HADN_C, false>(ar, sign_word_c, norm_c, sr_seed_c, gb, wc);
-                *reinterpret_cast<uint4*>(codes_c + row * (cols / 2) + cb / 2) =
+                *reinterpret_cast<uint4*>(codes_c + tiled_offset(row, cb / 32, cols / 32)) =
                     make_uint4(wc[0], wc[1], wc[2], wc[3]);
                 const int64_t blk = cb / 32;
                 scales_c[((blk >> 3) * rows + row) * 8 + (blk & 7)] = (uint8_t)bc;
@@ -519,12 +538,15 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
         *reinterpret_cast<uint4*>(stg + tid * kStageRow + 16 * t) =
             make_uint4(wd[t][0], wd[t][1], wd[t][2], wd[t][3]);
     __syncthreads();
+    // lane = 32 chunk + (column mod 32): with TB = 2 the two chunks of a
+    // 32-column group are adjacent 512-byte chunks of the tiled layout, so
+    // each store instruction writes 1 KB contiguous
 #pragma unroll
     for (int i = 0; i < TB; ++i) {
-        const int c = wave * 64 + i * (64 / TB) + lane / TB, chunk = lane % TB;
+        const int c = wave * 64 + i * 32 + (lane & 31), chunk = lane >> 5;
         const uint4 v = *reinterpret_cast<const uint4*>(stg + c * kStageRow + 16 * chunk);
         if (chunk < nt && c0 + c < cols)
-            *reinterpret_cast<uint4*>(codes + (c0 + c) * (rows / 2) + (rb0 + chunk) * 16) = v;
+            *reinterpret_cast<uint4*>(codes + tiled_offset(c0 + c, rb0 + chunk, nrb)) = v;
     }
     if (col >= cols) return;
     // rb0 is a multiple of TB: blocks rb0 .. rb0+TB-1 lie in one k-group
@@ -541,12 +563,9 @@ __global__ __launch_bounds__(kTileCols) void quant_mx_along_rows_lds(
 template <int HADN, bool SR>
 hipError_t launch_cols(const void* x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
                        uint64_t sr_seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
-    const int64_t nchunks = rows * cols / 8;
-    const int64_t per_block = (int64_t)kColsThreads * kColsUnroll;
-    const int64_t blocks = (nchunks + per_block - 1) / per_block;
-    hipLaunchKernelGGL((quant_mx_along_cols<HADN, SR>), dim3((unsigned)blocks), dim3(kColsThreads),
-                       0, st, (const uint4*)x, nchunks, sign_word, norm, sr_seed,
-                       (uint32_t*)codes, scales, cols / 32, rows, 1.0 / (double)(cols / 32));
+    const int64_t blocks = ((cols + 255) / 256) * ((rows + 31) / 32);
+    hipLaunchKernelGGL((quant_mx_along_cols<HADN, SR>), dim3((unsigned)blocks), dim3(kColsThreads), 0, st,
+                       (const uint16_t*)x, rows, cols, sign_word, norm, sr_seed, codes, scales);
     return hipGetLastError();
 }
 

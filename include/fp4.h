@@ -64,21 +64,45 @@ typedef enum {
 /* Which axis of x[rows, cols] the 32-element blocks run along (the GEMM
  * contraction axis of that operand). */
 typedef enum {
-    FP4_AXIS_COLS = 0,   /* blocks along cols (contiguous): codes [rows, cols/2],
-                            rows x cols/32 scales                               */
-    FP4_AXIS_ROWS = 1    /* blocks along rows (strided), i.e. quantize x^T:
-                            codes [cols, rows/2], cols x rows/32 scales         */
+    FP4_AXIS_COLS = 0,   /* blocks along cols (contiguous): an operand of R = rows
+                            rows of C = cols elements                           */
+    FP4_AXIS_ROWS = 1    /* blocks along rows (strided), i.e. quantize x^T: an
+                            operand of R = cols rows of C = rows elements       */
 } fp4_axis;
 
-/* MXFP4 scale layout ("k-grouped"), used by every MXFP4 entry point.  The
- * E8M0 scales of an operand with R logical rows and nb = C/32 blocks per row
- * are stored in groups of 8 consecutive blocks: the byte of block b of row r
- * is at offset ((b / 8) * R + r) * 8 + b % 8, i.e. an array [ceil(nb/8)][R][8]
+/* MXFP4 operand layouts, used by every MXFP4 entry point.  An operand has R
+ * logical rows of C contraction elements (C % 32 == 0), nb = C / 32 blocks
+ * per row.  Neither layout is the plain row-major [R, C/2] / [R, C/32]; the
+ * tags below name them, so that a caller can check at compile time
+ * (#if !FP4_CODE_LAYOUT_TILED32 ... #error) which layouts it was written for.
+ *
+ * Codes ("32-row tiled", FP4_CODE_LAYOUT_TILED32): the 16 code bytes of
+ * block b of row r (two E2M1 codes per byte, the even element in the low
+ * nibble) are at offset ((r / 32) * nb + b) * 512 + (r % 32) * 16, i.e. for
+ * each group of 32 rows and each block one contiguous 512-byte chunk, an
+ * array [ceil(R/32)][nb][32][16] of FP4_CODE_BYTES(R, C) bytes.  Two
+ * consecutive chunks of a row group are exactly the operand of one
+ * 32 x 32 x 64 scaled MFMA in lane order, so a GEMM loads each k-step of 32
+ * rows as one contiguous kilobyte.  When R % 32 != 0 the rows of the last
+ * group past R are padding: the quantizers do not write them and the GEMMs
+ * use them only for output rows that are not stored.
+ *
+ * Scales ("k-grouped", FP4_SCALE_LAYOUT_KGROUPED): the E8M0 scales are
+ * stored in groups of 8 consecutive blocks: the byte of block b of row r is
+ * at offset ((b / 8) * R + r) * 8 + b % 8, i.e. an array [ceil(nb/8)][R][8]
  * of FP4_SCALE_BYTES(R, C) bytes.  One group is the 256-element contraction
  * slice a GEMM stage consumes, so a stage's scales for consecutive rows are
  * one contiguous run.  When nb % 8 != 0 the last group's bytes past block
- * nb - 1 are padding: the quantizer does not write them and the GEMMs ignore
- * them. */
+ * nb - 1 are padding: the quantizers do not write them and the GEMMs ignore
+ * them.
+ *
+ * Output buffers are raw pointers: the library cannot check their extent.
+ * Codes and scales buffers must be at least FP4_CODE_BYTES(R, C) and
+ * FP4_SCALE_BYTES(R, C) bytes for the (R, C) of the call (a smaller buffer
+ * is written past its end). */
+#define FP4_CODE_LAYOUT_TILED32 1
+#define FP4_SCALE_LAYOUT_KGROUPED 1
+#define FP4_CODE_BYTES(R, C) ((((int64_t)(R) + 31) / 32) * 16 * (int64_t)(C))
 #define FP4_SCALE_BYTES(R, C) ((((int64_t)(C) / 32 + 7) / 8) * (int64_t)(R) * 8)
 
 /* Block rotation applied before quantization, along the block axis.
@@ -115,9 +139,9 @@ typedef enum {
  *      Philox4x32-10(key = sr_seed, counter = (idx >> 2, 0, 0) as 32-bit words
  *      (lo, hi, 0, 0)), idx = r * C + c the element's position in [R, C].
  *   4. codes: two per byte, the even element in the low nibble.
- * Output layout: codes [R, C/2] and the k-grouped scales of R rows of C/32
- * blocks (FP4_SCALE_BYTES(R, C) bytes), with (R, C) = (rows, cols) for
- * AXIS_COLS and (cols, rows) for AXIS_ROWS.
+ * Output layout: the tiled codes (FP4_CODE_BYTES(R, C) bytes) and the
+ * k-grouped scales (FP4_SCALE_BYTES(R, C) bytes) of R rows of C elements,
+ * with (R, C) = (rows, cols) for AXIS_COLS and (cols, rows) for AXIS_ROWS.
  * Requirements: C % 32 == 0; x, codes, scales 16-byte aligned.
  * had_n is ignored when had == FP4_HAD_NONE; sign_seed is ignored unless
  * SIGNED; sr_seed is ignored unless rnd == FP4_SR.  For Wgrad, quantize dY
@@ -173,9 +197,8 @@ fp4_status fp4_wgrad_quantize(const void* dy_bf16, const void* x_bf16, int64_t T
  * Dgrad dX = dY W, Wgrad dW = dY^T X, all in MXFP4 on native FP4 matrix
  * cores.  Each computes, in fp32 accumulation,
  *     C[m, n] = sum_k  e2m1(a[m,k]) 2^(sa[m,k/32]-127) * e2m1(b[n,k]) 2^(sb[n,k/32]-127)
- * over two MXFP4 operands stored along their contraction axis (codes [rows,
- * Kc/2] and k-grouped scales of rows x Kc/32 blocks, as fp4_hadamard_quantize
- * writes them).  C is
+ * over two MXFP4 operands stored along their contraction axis (tiled codes
+ * and k-grouped scales, as fp4_hadamard_quantize writes them).  C is
  * written (overwritten, not accumulated) as row-major fp32.
  * Requirements: T, N, K > 0; the contraction size a multiple of 32 and
  * below 2^24; at most 2^24 - 1 output tiles of 256 x 256; all pointers
@@ -206,7 +229,7 @@ typedef enum {
 /*
  * fp4_gemm_mx -- the same scaled-FP4 product as the three role entry points,
  * C[m, n] = sum_k a[m, k] b[n, k] over MXFP4 operands aq/as [M, Kc] and
- * bq/bs [N, Kc] (codes and k-grouped scales along the contraction, as
+ * bq/bs [N, Kc] (tiled codes and k-grouped scales along the contraction, as
  * fp4_hadamard_quantize writes them), with two output options:
  *   out = FP4_OUT_F32 or FP4_OUT_BF16: the element type of C (row-major
  *         [M, N]); bf16 is the fp32 result rounded to nearest even (NaN ->

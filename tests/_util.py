@@ -51,6 +51,26 @@ def ungroup_scales(g: np.ndarray, nb: int) -> np.ndarray:
     return np.ascontiguousarray(g.transpose(1, 0, 2).reshape(R, G * 8)[:, :nb])
 
 
+def tile_codes(c: np.ndarray, pad: int = 0) -> np.ndarray:
+    """Row-major MXFP4 codes [R, C/2] -> the library's 32-row tiled layout
+    [ceil(R/32), C/32, 512]: the 16 code bytes of row r, block b at
+    [r // 32, b, 16 (r % 32) .. + 16].  Rows past R (the padding of the last
+    row group) get `pad`."""
+    R, half = c.shape
+    nb = half // 16
+    G = (R + 31) // 32
+    p = np.full((G * 32, half), pad, dtype=np.uint8)
+    p[:R] = c
+    return np.ascontiguousarray(p.reshape(G, 32, nb, 16).transpose(0, 2, 1, 3).reshape(G, nb, 512))
+
+
+def untile_codes(t: np.ndarray, R: int) -> np.ndarray:
+    """The library's tiled codes [ceil(R/32), C/32, 512] -> row-major
+    [R, C/2] (drops the padding rows)."""
+    G, nb, _ = t.shape
+    return np.ascontiguousarray(t.reshape(G, nb, 32, 16).transpose(0, 2, 1, 3).reshape(G * 32, nb * 16)[:R])
+
+
 def sentinel_u8(shape) -> torch.Tensor:
     return torch.full(shape, 0xCD, dtype=torch.uint8, device="cuda")
 

@@ -200,9 +200,10 @@ def test_grouped_scale_layout_helpers():
             assert flat[((b // 8) * R + r) * 8 + b % 8] == s[r, b]
     assert (g[1, :, nb - 8:] == 0xFF).all()
     assert np.array_equal(ungroup_scales(g, nb), s)
-    assert F.mx_shapes(64, 416, F.AXIS_COLS) == ((64, 208), (2, 64, 8))
-    assert F.mx_shapes(416, 64, F.AXIS_ROWS) == ((64, 208), (2, 64, 8))
-    assert F.mx_shapes(3, 256, F.AXIS_COLS)[1] == (1, 3, 8)
+    assert F.mx_shapes(64, 416, F.AXIS_COLS) == ((2, 13, 512), (2, 64, 8))
+    assert F.mx_shapes(416, 64, F.AXIS_ROWS) == ((2, 13, 512), (2, 64, 8))
+    assert F.mx_shapes(3, 256, F.AXIS_COLS) == ((1, 8, 512), (1, 3, 8))
+    assert F.mx_shapes(33, 96, F.AXIS_COLS)[0] == (2, 3, 512)
 
 
 def test_binding_checks_output_extents():

@@ -51,7 +51,7 @@ def test_hip_quantizers_match_golden():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import fp4_precision_gemms_amd as F
-    from _util import say, sentinel_u8, to_gpu_bf16, ungroup_scales
+    from _util import say, sentinel_u8, to_gpu_bf16, ungroup_scales, untile_codes
 
     for had_name, had in HAD.items():
         sel = [c for c in CASES if c[1] == had]
@@ -66,7 +66,8 @@ def test_hip_quantizers_match_golden():
             F.fp4_hadamard_quantize(to_gpu_bf16(x), axis, 32, {O.HAD_NONE: F.HAD_NONE,
                                     O.HAD_DET: F.HAD_DET}[had], 0, F.RTN, 0, codes, scales)
             torch.cuda.synchronize()
-            codes, scales = codes.cpu().numpy(), ungroup_scales(scales.cpu().numpy(), 1)
+            codes = untile_codes(codes.cpu().numpy(), len(sel) * reps)
+            scales = ungroup_scales(scales.cpu().numpy(), 1)
             for i, (cid, _, _, scale, want, _) in enumerate(sel):
                 for r in range(reps):
                     row = i * reps + r

@@ -9,7 +9,7 @@ import torch
 import fp4_precision_gemms_amd as F
 import oracle as O
 import workloads as W
-from _util import gemm_check, group_scales, need_gpu, say, to_gpu_u8
+from _util import gemm_check, group_scales, need_gpu, say, tile_codes, to_gpu_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -23,11 +23,13 @@ def rand_operands(rng, rows, K, lo=112, hi=142):
 
 
 def run(fn, ops, out_shape):
-    """ops = (a codes, a scales, b codes, b scales), scales row-major [rows,
-    K/32]; the scales go to the GPU k-grouped with NaN-scale padding."""
+    """ops = (a codes, a scales, b codes, b scales) as the oracle writes them
+    (codes [rows, K/2], scales [rows, K/32]); they go to the GPU in the
+    library's layouts: codes 32-row tiled (padding rows 0xCD), scales
+    k-grouped with NaN-scale padding."""
     need_gpu()
     aq, as_, bq, bs = ops
-    g = [to_gpu_u8(a) for a in (aq, group_scales(as_), bq, group_scales(bs))]
+    g = [to_gpu_u8(a) for a in (tile_codes(aq, 0xCD), group_scales(as_), tile_codes(bq, 0xCD), group_scales(bs))]
     out = torch.full(out_shape, float("nan"), dtype=torch.float32, device="cuda")
     fn(*g, out=out)
     torch.cuda.synchronize()

@@ -13,7 +13,7 @@ import torch
 
 import fp4_precision_gemms_amd as F
 import oracle as O
-from _util import gemm_check, group_scales, need_gpu, say, to_gpu_u8
+from _util import gemm_check, group_scales, need_gpu, say, tile_codes, to_gpu_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def operands(M, N, K, seed):
 
 def run(aq, as_, bq, bs, out, dtype, acc):
     need_gpu()
-    g = [to_gpu_u8(a) for a in (aq, group_scales(as_), bq, group_scales(bs))]
+    g = [to_gpu_u8(a) for a in (tile_codes(aq, 0xCD), group_scales(as_), tile_codes(bq, 0xCD), group_scales(bs))]
     F.fp4_gemm_mx(*g, out=out, out_dtype=dtype, accumulate=acc)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()
@@ -103,7 +103,7 @@ def test_role_entry_points_equal_gemm_mx():
     M, N, K = 300, 260, 1024
     rng, aq, as_, bq, bs = operands(M, N, K, 9)
     need_gpu()
-    g = [to_gpu_u8(a) for a in (aq, group_scales(as_), bq, group_scales(bs))]
+    g = [to_gpu_u8(a) for a in (tile_codes(aq, 0xCD), group_scales(as_), tile_codes(bq, 0xCD), group_scales(bs))]
     a = F.fp4_gemm_fprop(*g)
     b = F.fp4_gemm_mx(*g)
     torch.cuda.synchronize()

@@ -9,7 +9,7 @@ import torch
 import fp4_precision_gemms_amd as F
 import oracle as O
 import workloads as W
-from _util import bf16_bits, need_gpu, say, sentinel_u8, to_gpu_bf16, ungroup_scales
+from _util import bf16_bits, need_gpu, say, sentinel_u8, to_gpu_bf16, ungroup_scales, untile_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,8 @@ def gpu_quant(bits, axis, had, had_n, rnd, sign_seed=0, sr_seed=0):
     # the padding of the last k-group is never written
     tail = g[-1, :, nb - 8 * (g.shape[0] - 1):]
     assert (tail == 0xCD).all(), "quantizer wrote the scale padding"
-    return codes.cpu().numpy(), ungroup_scales(g, nb)
+    R = rows if axis == O.AXIS_COLS else cols
+    return untile_codes(codes.cpu().numpy(), R), ungroup_scales(g, nb)
 
 
 def assert_same(got, ref, what):
@@ -191,11 +192,11 @@ def test_quant_input_over_2gib():
     rq, rs, cq, cs = F.fp4_hadamard_quantize_dual(x, 32, F.HAD_SIGNED, 9, F.RTN, 0, 32, F.HAD_NONE)
     torch.cuda.synchronize()
     got = {
-        "rows": (codes.cpu().numpy(), ungroup_scales(scales.cpu().numpy(), rows // 32),
+        "rows": (untile_codes(codes.cpu().numpy(), cols), ungroup_scales(scales.cpu().numpy(), rows // 32),
                  (O.AXIS_ROWS, O.HAD_DET, 0)),
-        "dual rows": (rq.cpu().numpy(), ungroup_scales(rs.cpu().numpy(), rows // 32),
+        "dual rows": (untile_codes(rq.cpu().numpy(), cols), ungroup_scales(rs.cpu().numpy(), rows // 32),
                       (O.AXIS_ROWS, O.HAD_SIGNED, 9)),
-        "dual cols": (cq.cpu().numpy(), ungroup_scales(cs.cpu().numpy(), cols // 32),
+        "dual cols": (untile_codes(cq.cpu().numpy(), rows), ungroup_scales(cs.cpu().numpy(), cols // 32),
                       (O.AXIS_COLS, O.HAD_NONE, 0)),
     }
     for what, (gc, gs, (axis, had, seed)) in got.items():

@@ -11,7 +11,7 @@ import torch
 
 import fp4_precision_gemms_amd as F
 import oracle as O
-from _util import bf16_bits, gemm_check, group_scales, need_gpu, say, to_gpu_u8
+from _util import bf16_bits, gemm_check, group_scales, need_gpu, say, tile_codes, to_gpu_u8
 from test_gpu_quant_mx import AX, HD, RN, gpu_quant
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_sweep_quantize_then_gemm(seed):
     # the scaled product of the two quantized operands: C = A B^T
     aq, as_ = ref_a
     bq, bs = ref_b
-    g = [to_gpu_u8(t) for t in (aq, group_scales(as_), bq, group_scales(bs))]
+    g = [to_gpu_u8(t) for t in (tile_codes(aq, 0xCD), group_scales(as_), tile_codes(bq, 0xCD), group_scales(bs))]
     out = torch.full((aq.shape[0], bq.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
     F.fp4_gemm_mx(*g, out=out)
     torch.cuda.synchronize()

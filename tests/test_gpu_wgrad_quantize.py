@@ -9,7 +9,7 @@ import torch
 
 import fp4_precision_gemms_amd as F
 import oracle as O
-from _util import bf16_bits, need_gpu, say, sentinel_u8, to_gpu_bf16, ungroup_scales
+from _util import bf16_bits, need_gpu, say, sentinel_u8, to_gpu_bf16, ungroup_scales, untile_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -55,5 +55,5 @@ def test_pair_matches_oracle():
     torch.cuda.synchronize()
     for (c, s), bits, sr in (((got[0], got[1]), dyb, 8), ((got[2], got[3]), xb, 9)):
         want = O.quant_mx(bits, O.AXIS_ROWS, 32, O.HAD_SIGNED, 7, O.RND_SR, sr)
-        assert np.array_equal(c.cpu().numpy(), want[0])
+        assert np.array_equal(untile_codes(c.cpu().numpy(), bits.shape[1]), want[0])
         assert np.array_equal(ungroup_scales(s.cpu().numpy(), T // 32), want[1])
