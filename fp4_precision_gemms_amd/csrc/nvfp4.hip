@@ -118,6 +118,19 @@ __global__ __launch_bounds__(kThreads) void nv_amax(const uint4* __restrict__ x,
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
+// The tensor scale of an amax: A / 2688 (6 * 448), 1 for A = 0.  `valid` is
+// false when that is not a finite positive number (A NaN, infinite,
+// negative, or so small that A / 2688 is zero): the whole tensor is then
+// NaN -- tensor scale NaN, every block scale 0x7F (the E4M3 NaN), all codes
+// zero.  Non-finite inputs are a reading: the pages are silent on them.
+__device__ __forceinline__ float tensor_scale_of(float amax, bool& valid) {
+    const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;
+    valid = (__float_as_uint(s_t) & 0x7FFFFFFFu) < 0x7F800000u && s_t > 0.0f;
+    return s_t;
+}
+constexpr uint32_t kQNaN = 0x7FC00000u;
+constexpr uint32_t kE4m3NaN = 0x7Fu;
+
 // E2M1 codes of 8 binary32 values, nearest with ties to even, saturating at
 // 6: V_CVT_SCALEF32_PK_FP4_F32 with scale 1 -- the same rounding as the MX
 // quantizers' hardware path (there checked bit-exact against the integer
@@ -148,10 +161,10 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
     uint64_t sr_seed, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tensor_scale) {
     static_assert(MODE == 0 || MODE == 2, "RTN or element SR");
-    const float amax = *amax_p;
-    const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;   // 6 * 448
+    bool valid;
+    const float s_t = tensor_scale_of(*amax_p, valid);
     const float six_st = 6.0f * s_t;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = valid ? s_t : __uint_as_float(kQNaN);
     const int q = threadIdx.x & 1;
     // Lanes 2p, 2p+1 hold the two 8-element halves of one block; chunk u of
     // a thread is kThreads chunks after chunk u - 1 (every load instruction
@@ -175,10 +188,15 @@ __global__ __launch_bounds__(kThreads) void nv_quant(
 #pragma unroll
         for (int t = 0; t < 8; ++t) m = max(m, __float_as_uint(y[t]) & 0x7FFFFFFFu);
         m = max(m, pair_xor1(m));
-        const uint32_t sb = e4m3_rne(__uint_as_float(m) / six_st);
+        // a NaN or infinite element in the block (m >= the infinity's bits),
+        // or a NaN tensor: scale 0x7F, codes zero
+        const bool bad = !valid || m >= 0x7F800000u;
+        const uint32_t sb = bad ? kE4m3NaN : e4m3_rne(__uint_as_float(m) / six_st);
         uint32_t word = 0;
-        if (sb != 0u) {
-            const float inv = 1.0f / (e4m3_value(sb) * s_t);
+        const float inv = 1.0f / (e4m3_value(sb) * s_t);
+        // (an infinite reciprocal -- s_b s_t below about 2^-128 -- gives zero
+        // codes and keeps s_b)
+        if (!bad && sb != 0u && __float_as_uint(inv) != 0x7F800000u) {
             float v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[t] = y[t] * inv;
@@ -225,10 +243,10 @@ __global__ __launch_bounds__(kThreads) void nv_quant_renorm(
     const uint4* __restrict__ x, int64_t nblocks, uint32_t sign_word, const float* __restrict__ amax_p,
     uint64_t sr_seed, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tensor_scale) {
-    const float amax = *amax_p;
-    const float s_t = amax == 0.0f ? 1.0f : amax / 2688.0f;   // 6 * 448
+    bool valid;
+    const float s_t = tensor_scale_of(*amax_p, valid);
     const float six_st = 6.0f * s_t;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = valid ? s_t : __uint_as_float(kQNaN);
     const int lane = threadIdx.x & 63;
     const int64_t b0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 256;
     uint4 wv[2 * kUnroll];
@@ -274,10 +292,13 @@ __global__ __launch_bounds__(kThreads) void nv_quant_renorm(
         uint32_t m = 0;
 #pragma unroll
         for (int t = 0; t < 16; ++t) m = max(m, __float_as_uint(y[t]) & 0x7FFFFFFFu);
-        const uint32_t sb = e4m3_rne(__uint_as_float(m) / six_st);
+        // as in nv_quant: a non-finite block or tensor gives 0x7F and zero
+        // codes, an infinite reciprocal scale zero codes with s_b kept
+        const bool bad = !valid || m >= 0x7F800000u;
+        const uint32_t sb = bad ? kE4m3NaN : e4m3_rne(__uint_as_float(m) / six_st);
         uint32_t c0 = 0, c1 = 0, stored = sb;
-        if (sb != 0u) {
-            const float inv = 1.0f / (e4m3_value(sb) * s_t);
+        const float inv = 1.0f / (e4m3_value(sb) * s_t);
+        if (!bad && sb != 0u && __float_as_uint(inv) != 0x7F800000u) {
             float v[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) v[t] = y[t] * inv;
@@ -292,7 +313,13 @@ __global__ __launch_bounds__(kThreads) void nv_quant_renorm(
                 num = fmaf(y[t], y[t], num);
                 den = fmaf(y[t], yq[t], den);
             }
-            if (den > 0.0f) stored = e4m3_sr(num / (s_t * den), srw[u]);
+            // the renormalized scale needs den > 0 and a target that is a
+            // number (Inf / Inf when the sums overflow keeps s_b; an
+            // infinite target saturates at 448)
+            if (den > 0.0f) {
+                const float target = num / (s_t * den);
+                if (target == target) stored = e4m3_sr(target, srw[u]);
+            }
         }
         codes[blk] = make_uint2(c0, c1);
         scales[blk] = (uint8_t)stored;

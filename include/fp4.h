@@ -289,8 +289,20 @@ typedef enum {
  * Layout: codes [rows, cols/2], scales_e4m3 [rows, cols/16].
  * workspace: device memory of nvfp4_workspace_bytes() bytes, used for the
  * tensor amax when amax_in == NULL (cleared by the library on `stream`);
- * may be NULL when amax_in != NULL.  NaN or infinite inputs give
- * unspecified codes and scales.
+ * may be NULL when amax_in != NULL.
+ * Non-finite values (the pages are silent; this is the library's rule):
+ *   - the computed A is NaN if any rotated element is NaN, else +Inf if any
+ *     is infinite;
+ *   - an A (computed or supplied) whose s_t is not a finite positive number
+ *     (A NaN, infinite, negative, or so small that A / 2688 is zero) makes
+ *     *tensor_scale the quiet NaN 0x7FC00000, every scale byte 0x7F (the
+ *     E4M3 NaN) and every code zero;
+ *   - otherwise a block holding a NaN or an infinity (also one produced by
+ *     the rotation) gets scale 0x7F and zero codes;
+ *   - a block whose fl(1 / fl(s_b s_t)) is infinite (A below about 2^-125)
+ *     gets zero codes and scale s_b;
+ *   - NVFP4_RENORM_SR keeps s_b when its target is NaN (sums that overflow)
+ *     and saturates an infinite target at 448.
  * Requirements: cols % 16 == 0; pointers 16-byte aligned (tensor_scale and
  * amax_in 4-byte aligned).
  */

@@ -457,7 +457,14 @@ float oracle_nvfp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int had,
  *   - the renormalization factor is per block, rho = |y|^2 / <y, y_hat>, and
  *     the stored scale is SR(s_b * rho) = SR(|y|^2 / (s_t * sum y_i q_i)) onto
  *     E4M3 with the purpose-2 stream at the block index; sums are binary32
- *     fmaf chains in element order.  A block with sum y_i q_i <= 0 keeps s_b.
+ *     fmaf chains in element order.  A block with sum y_i q_i <= 0, or whose
+ *     target is NaN, keeps s_b;
+ *   - non-finite values (the pages are silent): the tensor amax is NaN if any
+ *     rotated element is NaN, else infinite if any is; an amax without a
+ *     finite positive tensor scale makes every block scale 0x7F (E4M3 NaN),
+ *     every code zero and the tensor scale NaN; a block holding a NaN or an
+ *     infinity gets scale 0x7F and zero codes; a block whose reciprocal
+ *     scale 1 / (s_b s_t) overflows gets zero codes and scale s_b.
  * mode: 0 = elements to nearest, scale s_b; 1 = elements to nearest, scale
  * renormalized as above; 2 = every element rounded stochastically instead
  * ([QUARTET-II]: the recipe it compares against rounds each FP4 element
@@ -478,10 +485,21 @@ int oracle_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int had
     if (had != HAD_NONE) oracle_hadamard_signs(had, 16, sign_seed, signs);
     float amax = amax_in ? *amax_in : oracle_nvfp4_amax(x, rows, cols, had, sign_seed);
     float s_t = (amax == 0.0f) ? 1.0f : amax / 2688.0f;   /* 2688 = 6 * 448 */
-    *tensor_scale = s_t;
-    float six_st = 6.0f * s_t;
     int64_t nb = cols / 16;
     int64_t r;
+    /* Reading for non-finite inputs (the pages are silent): an amax that
+     * gives no finite positive tensor scale (NaN, infinite, negative, or so
+     * small that A / 2688 is zero) makes the whole tensor NaN: tensor scale
+     * NaN, every block scale the E4M3 NaN byte 0x7F, all codes zero. */
+    if (!(isfinite(s_t) && s_t > 0.0f)) {
+        uint32_t qnan = 0x7FC00000u;
+        memcpy(tensor_scale, &qnan, sizeof qnan);
+        memset(codes, 0, (size_t)(rows * (cols / 2)));
+        memset(scales, 0x7F, (size_t)(rows * nb));
+        return 0;
+    }
+    *tensor_scale = s_t;
+    float six_st = 6.0f * s_t;
 #pragma omp parallel for schedule(dynamic, 1)
     for (r = 0; r < rows; ++r) {
         float y[16];
@@ -489,10 +507,19 @@ int oracle_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int had
         for (int64_t b = 0; b < nb; ++b) {
             for (int i = 0; i < 16; ++i) y[i] = oracle_bf16_to_f32(x[r * cols + b * 16 + i]);
             if (had != HAD_NONE) oracle_fwht(y, 16, signs);
+            uint8_t* crow = codes + r * (cols / 2) + b * 8;
+            /* a block holding a NaN or an infinity (also one the rotation
+             * produced): scale 0x7F (E4M3 NaN), codes zero */
+            int finite = 1;
+            for (int i = 0; i < 16; ++i) finite &= isfinite(y[i]) != 0;
+            if (!finite) {
+                memset(crow, 0, 8);
+                scales[r * nb + b] = 0x7F;
+                continue;
+            }
             float m = 0.0f;
             for (int i = 0; i < 16; ++i) { float a = fabsf(y[i]); if (a > m) m = a; }
             uint8_t sb = oracle_e4m3_rne(m / six_st);
-            uint8_t* crow = codes + r * (cols / 2) + b * 8;
             if (sb == 0) {
                 memset(crow, 0, 8);
                 scales[r * nb + b] = 0;
@@ -500,6 +527,15 @@ int oracle_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int had
             }
             float sbf = (float)oracle_e4m3_decode(sb);
             float inv = 1.0f / (sbf * s_t);
+            /* the reciprocal of the block's scale overflows (a tensor amax
+             * below about 2^-125 puts s_b s_t under 2^-128): the codes are
+             * zero and the scale stays s_b -- every value such a block
+             * dequantizes to is below the binary32 normal range */
+            if (isinf(inv)) {
+                memset(crow, 0, 8);
+                scales[r * nb + b] = sb;
+                continue;
+            }
             for (int i = 0; i < 16; ++i) {
                 float v = y[i] * inv;
                 if (mode == 2) {
@@ -517,10 +553,15 @@ int oracle_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int had
                     num = fmaf(y[i], y[i], num);
                     den = fmaf(y[i], (float)oracle_e2m1_decode(q[i]), den);
                 }
+                /* the renormalized scale needs den > 0 and a target that is
+                 * a number (sums of squares of values near the binary32 limit
+                 * overflow; Inf / Inf keeps s_b, an infinite target saturates
+                 * at 448) */
                 if (den > 0.0f) {
                     float target = num / (s_t * den);
                     uint64_t blk = (uint64_t)r * (uint64_t)nb + (uint64_t)b;
-                    stored = oracle_e4m3_sr(target, oracle_stream_word(sr_seed, 2, blk));
+                    if (!isnan(target))
+                        stored = oracle_e4m3_sr(target, oracle_stream_word(sr_seed, 2, blk));
                 }
             }
             scales[r * nb + b] = stored;

@@ -68,3 +68,57 @@ def test_nvfp4_full_size():
     bits = W.tensor(w, "x")
     check(bits, O.HAD_SIGNED, 123, O.NV_RENORM_SR, 77, what="full")
     check(bits, O.HAD_SIGNED, 123, O.NV_ELEMENT_SR, 77, what="full element SR")
+
+
+MODES = [O.NV_RTN, O.NV_RENORM_SR, O.NV_ELEMENT_SR]
+
+
+def _edge_tensor():
+    """Finite blocks, a NaN, +-Inf, a block whose 16-point rotation overflows,
+    values near the binary32 limit (renorm sums overflow) and tiny ones."""
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((12, 96)).astype(np.float32)
+    v[0, 3] = np.nan
+    v[2, 40] = np.inf
+    v[3, 70] = -np.inf
+    v[5, 16:32] = 3.0e38                   # finite; the rotation overflows
+    v[7, 48:64] = -3.0e38
+    v[9, :16] = 1e-38
+    return v
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("had", [O.HAD_NONE, O.HAD_SIGNED])
+def test_nvfp4_nonfinite_inputs(mode, had):
+    """The library's rule for non-finite values, bit-exact against the
+    oracle: with the amax computed, a NaN or infinity anywhere makes the
+    whole tensor NaN; with it supplied, only the affected blocks get scale
+    0x7F and zero codes."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        bits = bf16_bits(_edge_tensor())
+    check(bits, had, 3, mode, 8, what="nonfinite computed amax")
+    check(bits, had, 3, mode, 8, amax_in=5.0, what="nonfinite amax_in")
+    check(bits, had, 3, mode, 8, amax_in=3.0e38, what="nonfinite huge amax_in")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("amax", [float("nan"), float("inf"), -1.0, 1e-45, 0.0])
+def test_nvfp4_invalid_amax_in(mode, amax):
+    rng = np.random.default_rng(22)
+    bits = bf16_bits(rng.standard_t(4, (8, 64)))
+    check(bits, O.HAD_SIGNED, 4, mode, 9, amax_in=amax, what="amax_in %r" % amax)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("had", [O.HAD_NONE, O.HAD_DET])
+def test_nvfp4_tiny_and_huge_tensors(mode, had):
+    """A tensor near 2^-127 (reciprocal block scales overflow) and one near
+    3e38 (the renormalized target can be Inf / Inf), each whole."""
+    rng = np.random.default_rng(23)
+    tiny = (rng.uniform(0.5, 1.0, (8, 64)) * 2.0 ** -127).astype(np.float32)
+    tiny[7] *= 2.0 ** 8
+    huge = (rng.standard_normal((8, 64)) * 1e37).astype(np.float32)
+    huge[0, :16] = 3.0e38
+    check(bf16_bits(tiny), had, 2, mode, 6, what="tiny")
+    check(bf16_bits(huge), had, 2, mode, 6, what="huge")
+    check(bf16_bits(tiny), had, 2, mode, 6, amax_in=1e-40, what="tiny, small amax_in")

@@ -226,3 +226,120 @@ def test_total_error_half_of_element_sr():
         me += np.mean((dequant(ce, se, st) - y) ** 2)
         mr += np.mean((dequant(cr, sr, st) - y) ** 2)
     assert 1.6 < me / mr < 2.4
+
+
+# --- non-finite and extreme inputs (a reading: the pages are silent) --------
+
+NAN_BITS = 0x7FC00000
+MODES = [O.NV_RTN, O.NV_RENORM_SR, O.NV_ELEMENT_SR]
+
+
+def _nan_tensor(c, s, st):
+    return (np.float32(st).view(np.uint32) == NAN_BITS and not c.any() and (s == 0x7F).all())
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("had", [O.HAD_NONE, O.HAD_SIGNED])
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_nonfinite_element_makes_computed_amax_tensor_nan(mode, had, bad):
+    """A NaN or an infinity anywhere gives a non-finite tensor amax: the
+    whole tensor is NaN (tensor scale NaN, every scale byte 0x7F, codes 0)."""
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((8, 64)).astype(np.float32)
+    v[5, 17] = bad
+    x = bf16(v)
+    amax = O.nvfp4_amax(x, had, 2)
+    assert np.isnan(amax) if np.isnan(bad) else np.isinf(amax)
+    assert _nan_tensor(*O.nvfp4_quantize(x, had, 2, mode, 9))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("amax", [np.nan, np.inf, -1.0, -0.5e-30, 1e-45])
+def test_invalid_amax_in_makes_tensor_nan(mode, amax):
+    """A supplied amax without a finite positive tensor scale (NaN, infinite,
+    negative, or so small that amax / 2688 is zero in binary32)."""
+    x = bf16(np.random.default_rng(4).standard_normal((4, 32)))
+    assert np.float32(np.float32(1e-45) / np.float32(2688.0)) == 0.0
+    assert _nan_tensor(*O.nvfp4_quantize(x, O.HAD_SIGNED, 1, mode, 2, amax_in=amax))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("had", [O.HAD_NONE, O.HAD_DET, O.HAD_SIGNED])
+def test_nonfinite_block_with_supplied_amax(mode, had):
+    """With the amax supplied the blocks are independent: a block holding a
+    NaN, an infinity, or values whose rotation overflows gets scale 0x7F and
+    zero codes, and every other block is exactly what the same tensor with
+    finite values in those blocks gives."""
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((6, 64)).astype(np.float32)
+    bad = v.copy()
+    bad[0, 3] = np.nan                    # block (0, 0)
+    bad[2, 40] = -np.inf                  # block (2, 2)
+    bad[4, 48:64] = 3.0e38                # block (4, 3): finite, but 16 * 3e38 overflows
+    x_bad, x_ok = bf16(bad), bf16(v)
+    cb, sb, tb = O.nvfp4_quantize(x_bad, had, 7, mode, 3, amax_in=5.0)
+    co, so, to = O.nvfp4_quantize(x_ok, had, 7, mode, 3, amax_in=5.0)
+    assert tb == to == np.float32(5.0) / np.float32(2688.0)
+    bad_blocks = [(0, 0), (2, 2)] + ([(4, 3)] if had != O.HAD_NONE else [])
+    keep = np.ones(sb.shape, bool)
+    for r, b in bad_blocks:
+        assert sb[r, b] == 0x7F and not cb[r, 8 * b:8 * b + 8].any(), (r, b)
+        keep[r, b] = False
+    if had == O.HAD_NONE:        # 3e38 is finite and unrotated: a saturated scale
+        keep[4, 3] = False
+        assert sb[4, 3] == 0x7E
+    assert np.array_equal(sb[keep], so[keep])
+    kc = np.repeat(keep, 8, axis=1)
+    assert np.array_equal(cb[kc], co[kc])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_reciprocal_scale_overflow_gives_zero_codes(mode):
+    """A tensor with amax near 2^-127: for blocks whose s_b s_t is below
+    about 2^-128, fl(1 / fl(s_b s_t)) is infinite in binary32 (recomputed
+    here with numpy and torch's E4M3 cast); those blocks get zero codes and
+    scale s_b, the others are ordinary (some nonzero code)."""
+    rng = np.random.default_rng(6)
+    v = (rng.uniform(0.5, 1.0, (4, 64)) * 2.0 ** -127).astype(np.float32)
+    v[3] *= 2.0 ** 8                       # row 3: normal values, amax 2^-119 .. 2^-120
+    x = bf16(v)
+    y = f32(x)
+    c, s, st = O.nvfp4_quantize(x, O.HAD_NONE, 0, mode, 5)
+    A = np.float32(np.abs(y).max())
+    assert st == A / np.float32(2688.0)
+    hits = [0, 0]
+    for r in range(4):
+        for b in range(4):
+            m = np.float32(np.abs(y[r, 16 * b:16 * b + 16]).max())
+            sbv = torch.tensor([float(m / (np.float32(6.0) * st))]).to(torch.float8_e4m3fn).float().item()
+            code = int(torch.tensor([sbv]).to(torch.float8_e4m3fn).view(torch.uint8).item())
+            with np.errstate(over="ignore", divide="ignore"):
+                inv = np.float32(1.0) / (np.float32(sbv) * st)
+            if mode != O.NV_RENORM_SR:
+                assert s[r, b] == code, (r, b)
+            hits[int(np.isinf(inv))] += 1
+            if np.isinf(inv):
+                assert not c[r, 8 * b:8 * b + 8].any() and s[r, b] == code, (r, b)
+            else:
+                assert c[r, 8 * b:8 * b + 8].any(), (r, b)
+    assert hits[0] > 0 and hits[1] > 0        # both kinds of block occur
+
+
+def test_renorm_target_nan_keeps_block_scale():
+    """Values near the binary32 limit: sum y^2 and sum y q both overflow to
+    infinity, so the renormalized target is Inf / Inf; the block keeps its
+    round-to-nearest scale (mode 0's byte), the other blocks still move."""
+    rng = np.random.default_rng(8)
+    v = rng.standard_normal((2, 32)).astype(np.float32) * np.float32(1e37)
+    v[0, :16] = 3.0e38
+    x = bf16(v)
+    c0, s0, t0 = O.nvfp4_quantize(x, O.HAD_NONE, 0, O.NV_RTN, 1)
+    c1, s1, t1 = O.nvfp4_quantize(x, O.HAD_NONE, 0, O.NV_RENORM_SR, 1)
+    y = f32(x)[0, :16]
+    with np.errstate(over="ignore", invalid="ignore"):
+        num = np.float32(0)
+        for t in y:
+            num = np.float32(num + np.float32(t) * np.float32(t))
+    assert np.isinf(num)
+    assert s1[0, 0] == s0[0, 0] and t1 == t0
+    assert np.array_equal(c1, c0)
