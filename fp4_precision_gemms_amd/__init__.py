@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, u64, i32, u64, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
     L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize_noalloc.argtypes = [vp, i64, i64, i32, u64, i32, u64, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_noalloc.restype = i32
     L.nvfp4_workspace_bytes.argtypes = [i64, i64]
     L.nvfp4_workspace_bytes.restype = ctypes.c_size_t
     L.fp4_status_string.argtypes = [i32]
@@ -312,6 +314,32 @@ def nvfp4_quantize(x: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0, m
                                 scales.data_ptr(), tensor_scale.data_ptr(), _ptr(workspace),
                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                 _stream_ptr(stream, dev)))
+    return codes, scales, tensor_scale
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                           tensor_scale: torch.Tensor, had: int = HAD_SIGNED, sign_seed: int = 0,
+                           mode: int = NV_RENORM_SR, sr_seed: int = 0,
+                           amax_in: torch.Tensor | None = None, stream=None):
+    """nvfp4_quantize into caller-provided outputs, with the in-library amax
+    in the library's own device scratch instead of a workspace (see
+    include/fp4.h: calls that overlap on one GPU race on it)."""
+    rows, cols = x.shape
+    for t, sh, dt, n in ((codes, (rows, cols // 2), torch.uint8, "codes"),
+                         (scales, (rows, cols // 16), torch.uint8, "scales"),
+                         (tensor_scale, (1,), torch.float32, "tensor_scale")):
+        if tuple(t.shape) != sh:
+            raise ValueError("%s must have shape %s, got %s" % (n, sh, tuple(t.shape)))
+        _need(t, dt, n)
+    _need(x, torch.bfloat16, "x")
+    if amax_in is not None:
+        if amax_in.numel() != 1:
+            raise ValueError("amax_in must hold one float")
+        _need(amax_in, torch.float32, "amax_in")
+    _check(lib().nvfp4_quantize_noalloc(x.data_ptr(), rows, cols, had, sign_seed & (2 ** 64 - 1), mode,
+                                        sr_seed & (2 ** 64 - 1), _ptr(amax_in), codes.data_ptr(),
+                                        scales.data_ptr(), tensor_scale.data_ptr(),
+                                        _stream_ptr(stream, x.device)))
     return codes, scales, tensor_scale
 
 

@@ -143,10 +143,10 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols) {
     return 256;   // one 32-bit amax word, padded to the allocation granule
 }
 
-fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
-                          uint64_t sign_seed, nvfp4_mode mode, uint64_t sr_seed, const float* amax_in,
-                          uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+fp4_status check_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
+                       nvfp4_mode mode, const float* amax_in, const uint8_t* codes,
+                       const uint8_t* scales_e4m3, const float* tensor_scale) {
     if (had != FP4_HAD_NONE && had != FP4_HAD_DET && had != FP4_HAD_SIGNED) return FP4_ERR_ENUM;
     if (mode != NVFP4_RTN && mode != NVFP4_RENORM_SR && mode != NVFP4_ELEMENT_SR) return FP4_ERR_ENUM;
     if (!x_bf16 || !codes || !scales_e4m3 || !tensor_scale) return FP4_ERR_NULL;
@@ -154,6 +154,17 @@ fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_ha
     if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales_e4m3) ||
         !aligned4(tensor_scale) || (amax_in && !aligned4(amax_in)))
         return FP4_ERR_ALIGN;
+    return FP4_OK;
+}
+}  // namespace
+
+fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
+                          uint64_t sign_seed, nvfp4_mode mode, uint64_t sr_seed, const float* amax_in,
+                          uint8_t* codes, uint8_t* scales_e4m3, float* tensor_scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    const fp4_status s = check_nvfp4(x_bf16, rows, cols, had, mode, amax_in, codes, scales_e4m3,
+                                     tensor_scale);
+    if (s != FP4_OK) return s;
     if (!amax_in) {
         if (!workspace || workspace_bytes < nvfp4_workspace_bytes(rows, cols))
             return FP4_ERR_WORKSPACE;
@@ -161,6 +172,25 @@ fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_ha
     }
     return from_hip(fp4dev::launch_nvfp4(x_bf16, rows, cols, (int)had, sign_seed, (int)mode, sr_seed,
                                          amax_in, codes, scales_e4m3, tensor_scale, workspace,
+                                         (hipStream_t)stream));
+}
+
+fp4_status nvfp4_quantize_noalloc(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
+                                  uint64_t sign_seed, nvfp4_mode mode, uint64_t sr_seed,
+                                  const float* amax_in, uint8_t* codes, uint8_t* scales_e4m3,
+                                  float* tensor_scale, void* stream) {
+    const fp4_status s = check_nvfp4(x_bf16, rows, cols, had, mode, amax_in, codes, scales_e4m3,
+                                     tensor_scale);
+    if (s != FP4_OK) return s;
+    void* ws = nullptr;
+    if (!amax_in) {
+        // the amax word in the library's per-device scratch array
+        size_t bytes = 0;
+        if (fp4dev::nvfp4_scratch(&ws, &bytes) != hipSuccess) return FP4_ERR_LAUNCH;
+        if (nvfp4_workspace_bytes(rows, cols) > bytes) return FP4_ERR_WORKSPACE;
+    }
+    return from_hip(fp4dev::launch_nvfp4(x_bf16, rows, cols, (int)had, sign_seed, (int)mode, sr_seed,
+                                         amax_in, codes, scales_e4m3, tensor_scale, ws,
                                          (hipStream_t)stream));
 }
 

@@ -41,6 +41,10 @@ hipError_t launch_nvfp4(const void* x, int64_t rows, int64_t cols, int had, uint
                         int mode, uint64_t sr_seed, const float* amax_in, uint8_t* codes,
                         uint8_t* scales, float* tensor_scale, void* workspace, hipStream_t st);
 
+// Device address and size of this device's scratch array (the current
+// device; looked up once per device, thread-safe).
+hipError_t nvfp4_scratch(void** ptr, size_t* bytes);
+
 uint32_t host_sign_word(int had, uint64_t seed);
 
 }  // namespace fp4dev

@@ -31,6 +31,17 @@
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
+#include <mutex>
+
+// Scratch memory of the allocation-free entry point (nvfp4_quantize_noalloc):
+// the in-library amax word, in a fixed device array instead of a workspace
+// the caller passes.  Each GPU the library runs on holds its own copy until
+// the process ends; every call on that GPU shares it (the amax pass clears
+// it with a kernel first), so calls that overlap on one GPU race.  In host
+// code `scratch` is only a symbol: kernels get its device address, looked
+// up once per device by nvfp4_scratch below.
+static __device__ __align__(256) uint32_t scratch[64];
+
 namespace fp4dev {
 namespace {
 
@@ -360,6 +371,27 @@ hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw,
 }
 
 }  // namespace
+
+hipError_t nvfp4_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // with `dev` current: this device's copy of the array
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = sizeof(scratch);
+    return hipSuccess;
+}
 
 hipError_t launch_nvfp4(const void* x, int64_t rows, int64_t cols, int had, uint64_t sign_seed,
                         int mode, uint64_t sr_seed, const float* amax_in, uint8_t* codes,

@@ -315,6 +315,28 @@ fp4_status nvfp4_quantize(const void* x_bf16, int64_t rows, int64_t cols, fp4_ha
 /* Workspace bytes nvfp4_quantize needs for a [rows, cols] input. */
 size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols);
 
+/*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as nvfp4_quantize; the in-library tensor amax (when
+ * amax_in == NULL) lives in a 256-byte array the library holds in device
+ * memory, one per GPU, until the process ends.  Nothing is allocated or
+ * freed by the call.
+ *   - The scratch array holds the one-word amax of an input of any size;
+ *     FP4_ERR_WORKSPACE if nvfp4_workspace_bytes(rows, cols) ever exceeded
+ *     its 256 bytes.
+ *   - Every call on one GPU shares that GPU's array (cleared by a kernel at
+ *     the start of each two-pass call): calls that overlap on one GPU, e.g.
+ *     on two streams, race on it and must be serialized by the caller.
+ *   - FP4_ERR_LAUNCH also reports a failure to look up the array's device
+ *     address (once per device, on the first call with it current).
+ */
+fp4_status nvfp4_quantize_noalloc(const void* x_bf16, int64_t rows, int64_t cols, fp4_hadamard had,
+                                  uint64_t sign_seed, nvfp4_mode mode, uint64_t sr_seed,
+                                  const float* amax_in, uint8_t* codes, uint8_t* scales_e4m3,
+                                  float* tensor_scale, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* fp4_status_string(fp4_status status);
 

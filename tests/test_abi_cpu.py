@@ -177,6 +177,24 @@ def test_nvfp4_errors(L):
     assert L.nvfp4_workspace_bytes(32, 64) >= 4
 
 
+def test_nvfp4_noalloc_errors(L):
+    """The allocation-free NVFP4 entry point checks its arguments like
+    nvfp4_quantize, before any HIP call."""
+    def call(x=A, rows=32, cols=64, had=2, mode=1, amax=None, codes=A, scales=A, ts=A):
+        return L.nvfp4_quantize_noalloc(x, rows, cols, had, 0, mode, 0, amax, codes, scales, ts, None)
+
+    assert call(had=5) == ERR_ENUM
+    assert call(mode=3) == ERR_ENUM
+    assert call(x=None) == ERR_NULL
+    assert call(codes=None) == ERR_NULL
+    assert call(ts=None) == ERR_NULL
+    assert call(cols=24) == ERR_SHAPE
+    assert call(rows=-1) == ERR_SHAPE
+    assert call(scales=MIS) == ERR_ALIGN
+    assert call(amax=A + 2) == ERR_ALIGN
+    assert "nvfp4_quantize_noalloc" in declared_functions()
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     if not os.path.exists(F.LIB_PATH):
