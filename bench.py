@@ -8,24 +8,32 @@ both operands in one fp4_wgrad_quantize launch), then dW[N, K] = dY^T X on
 the scaled FP4 matrix cores, fp32 output.  Inputs
 are synthetic bf16 tensors resident in HBM before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload gate_up|q_proj|down_proj]
+    python bench.py [--steps K] [--warmup W] [--settle-ms MS] [--flush]
+                    [--workload gate_up|q_proj|down_proj]
                     [--variant det-rtn|signed-rtn|signed-rtn-perstep|sr]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-mfma-ceiling] [--copy-calibration]
     python bench.py --counters FETCH_DIR WRITE_DIR     (no GPU: writes the summary)
     python bench.py --nvfp4                            (the secondary NVFP4 quantizer)
     python bench.py --layer [--workload W]             (the whole linear layer: three GEMMs)
     python bench.py --autograd [--workload W]          (MXFP4LinearFunction forward + backward, bf16)
     python bench.py --mfma-ceiling                     (only the MFMA-rate measurement aid)
 
-Prints one JSON line.  `value` is Wgrad TFLOP/s including quantization
-(2 T N K flops over the whole step, the K timed steps holding nothing but
-their launches); the roofline object describes the dominant kernel (the
-GEMM) from HIP events around each launch over a second pass of K steps;
-cpu_baseline times the plain CPU oracle on a bounded sample of the same
-workload; mfma_ceiling is the scaled FP4 MFMA rate the card sustains on
-random operands with no memory traffic at all (libfp4calib.so), measured
-after the timed steps, and the shader clock it ran at -- the bound the
-card's power limit puts on any GEMM on such data.
+Procedure: W warm-up steps, then back-to-back steps for --settle-ms
+milliseconds whatever W is (reported as "settle": the card's clocks take
+tens of milliseconds of load to settle), then the K timed steps holding
+nothing but their launches, with a clock-stamp kernel on either side
+(sclk_GHz_timed: the average shader clock over them).  Prints one JSON line.
+`value` is Wgrad TFLOP/s including quantization (2 T N K flops per step);
+the roofline object describes the dominant kernel (the GEMM) from HIP
+events around each launch over a second pass of K steps; breakdown holds
+both kernels and the card's device-to-device copy rate; --flush adds a pass
+with a 1 GiB write before each step (cold L2 and memory-side cache, median
+and minimum); cpu_baseline times the plain CPU oracle on a bounded sample of
+the same workload and checks the last timed step's outputs against it
+(timed_run_parity); mfma_ceiling is the scaled FP4 MFMA rate the card
+sustains on random operands with no memory traffic at all
+(libfp4calib.so), measured after the timed steps, and the shader clock it
+ran at -- the bound the card's power limit puts on any GEMM on such data.
 """
 from __future__ import annotations
 
@@ -147,33 +155,111 @@ def counter_summary(fetch_dir, write_dir):
     return 0
 
 
-def cpu_baseline(w, dY, X, variant="det-rtn"):
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def untile_codes(t, R):
+    """The library's 32-row tiled MXFP4 codes [ceil(R/32), C/32, 512] ->
+    row-major [R, C/2] (layout only)."""
+    G, nb, _ = t.shape
+    return t.reshape(G, nb, 32, 16).transpose(0, 2, 1, 3).reshape(G * 32, nb * 16)[:R]
+
+
+def ungroup_scales(g, nb):
+    """k-grouped scales [ceil(nb/8), R, 8] -> row-major [R, nb] (layout only)."""
+    G, R, _ = g.shape
+    return g.transpose(1, 0, 2).reshape(R, G * 8)[:, :nb]
+
+
+def step_settings(variant, i):
+    """(hadamard name, sign seed, rounding name, SR seeds) of step i."""
+    had_name, per_step_sign, rnd_name = VARIANTS[variant]
+    sign_seed = 1000 + i if per_step_sign else 7
+    seeds = (2 * i + 1, 2 * i + 2) if rnd_name.startswith("sr") else (0, 0)
+    return had_name, sign_seed, rnd_name, seeds
+
+
+def cpu_baseline(w, dY, X, variant="det-rtn", timed=None):
     """The oracle, untuned, on a bounded sample of the same Wgrad: the full
     rotation + MXFP4 quantization of dY and X along tokens (the variant's
-    transform and rounding, step 0's seeds), then 256 of dW's rows by the
-    binary64 oracle GEMM, scaled to all rows.  Returns the JSON object."""
+    transform and rounding, step 0's seeds), then as many of dW's rows by
+    the binary64 oracle GEMM as about 10 s allow (256 at a time), scaled to
+    all rows.  Returns the JSON object.
+
+    `timed` = (step index, dY^T codes, dY^T scales, X^T codes, X^T scales,
+    dW) copied to the host right after the timed steps: its codes and scales
+    are compared whole with the oracle's quantization under that step's
+    seeds, and 4096 entries of dW (corners, every 224/256-row tile edge,
+    random) with the oracle's binary64 product (|err| <= 1e-5 sum |a b|),
+    reported as "timed_run_parity"."""
+    import numpy as np
     import oracle as O
 
-    had_name, _, rnd_name = VARIANTS[variant]
-    had = {"deterministic-32": O.HAD_DET, "none": O.HAD_NONE}.get(had_name, O.HAD_SIGNED)
-    rnd = O.RND_SR if rnd_name.startswith("sr") else O.RND_RTN
-    sign_seed = 1000 if variant == "signed-rtn-perstep" else 7
-    seeds = (1, 2) if rnd == O.RND_SR else (0, 0)
-    n = 256
+    def settings(i):
+        had_name, sign_seed, rnd_name, seeds = step_settings(variant, i)
+        had = {"deterministic-32": O.HAD_DET, "none": O.HAD_NONE}.get(had_name, O.HAD_SIGNED)
+        rnd = O.RND_SR if rnd_name.startswith("sr") else O.RND_RTN
+        return had_name, had, sign_seed, rnd_name, rnd, seeds
+
+    had_name, had, sign_seed, rnd_name, rnd, seeds = settings(0)
     t0 = time.perf_counter()
     aq, as_ = O.quant_mx(dY, O.AXIS_ROWS, 32, had, sign_seed, rnd, seeds[0])
     bq, bs = O.quant_mx(X, O.AXIS_ROWS, 32, had, sign_seed, rnd, seeds[1])
     t1 = time.perf_counter()
-    O.gemm_rows(aq, as_, bq, bs, 0, n)
+    # dW rows in chunks of 256 until about 10 s of GEMM work
+    n = 0
+    while n < w.N and time.perf_counter() - t1 < 10.0:
+        O.gemm_rows(aq, as_, bq, bs, n, min(n + 256, w.N))
+        n = min(n + 256, w.N)
     t2 = time.perf_counter()
     t_full = (t1 - t0) + (t2 - t1) * w.N / n
     flops = 2.0 * w.T * w.N * w.K
-    return {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
-            "kind": "oracle",
-            "sample": "rotation (%s) + MXFP4 quantization (%s) of all of dY[%d x %d] and X[%d x %d] "
-                      "along tokens (%.1f s), then %d of %d dW rows by the binary64 oracle GEMM "
-                      "(%.1f s), GEMM time scaled by rows to the full layer (%.0f s total)"
-                      % (had_name, rnd_name, w.T, w.N, w.T, w.K, t1 - t0, n, w.N, t2 - t1, t_full)}
+    out = {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": O.num_threads(),
+           "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": "rotation (%s) + MXFP4 quantization (%s) of all of dY[%d x %d] and X[%d x %d] "
+                     "along tokens (%.1f s), then %d of %d dW rows by the binary64 oracle GEMM "
+                     "(%.1f s), GEMM time scaled by rows to the full layer (%.0f s total)"
+                     % (had_name, rnd_name, w.T, w.N, w.T, w.K, t1 - t0, n, w.N, t2 - t1, t_full)}
+    if timed is not None:
+        i, gq_dy, gs_dy, gq_x, gs_x, gdw = timed
+        _, had_i, sign_i, _, rnd_i, seeds_i = settings(i)
+        if (had_i, sign_i, rnd_i, seeds_i) != (had, sign_seed, rnd, seeds):
+            aq, as_ = O.quant_mx(dY, O.AXIS_ROWS, 32, had_i, sign_i, rnd_i, seeds_i[0])
+            bq, bs = O.quant_mx(X, O.AXIS_ROWS, 32, had_i, sign_i, rnd_i, seeds_i[1])
+        nb = w.T // 32
+        codes_ok = bool(np.array_equal(untile_codes(gq_dy, w.N), aq) and
+                        np.array_equal(untile_codes(gq_x, w.K), bq))
+        scales_ok = bool(np.array_equal(ungroup_scales(gs_dy, nb), as_) and
+                         np.array_equal(ungroup_scales(gs_x, nb), bs))
+        rng = np.random.default_rng(1)
+        M, N = w.N, w.K
+
+        def edges(n):
+            # both sides of every 224- and 256-wide tile boundary, and the ends
+            return np.array(sorted({0, n - 1} | {e for t in (224, 256) for k in range(1, n // t + 1)
+                                                 for e in (k * t - 1, k * t) if e < n}))
+
+        em, en = edges(M), edges(N)
+        nr = 4096 - em.size - en.size - 4
+        mi = np.concatenate([em, rng.integers(0, M, en.size), rng.integers(0, M, nr), [0, 0, M - 1, M - 1]])
+        ni = np.concatenate([rng.integers(0, N, em.size), en, rng.integers(0, N, nr), [0, N - 1, 0, N - 1]])
+        ref, mag = O.gemm_entries(aq, as_, bq, bs, mi, ni)
+        err = np.abs(gdw[mi, ni].astype(np.float64) - ref)
+        out["timed_run_parity"] = {
+            "step": i, "codes_bitexact": codes_ok, "scales_bitexact": scales_ok,
+            "dw_entries": int(mi.size), "dw_within_1e-5_sum_abs": bool((err <= 1e-5 * mag).all()),
+            "dw_max_err_over_sum_abs": float((err / np.maximum(mag, 1e-300)).max()),
+            "what": "the last timed step's dY^T and X^T codes and scales, whole, against the oracle "
+                    "under that step's seeds; 4096 dW entries against the binary64 oracle product"}
+    return out
 
 
 def nvfp4_bench(args) -> int:
@@ -376,13 +462,18 @@ def autograd_bench(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the card needs tens of milliseconds of load before its clocks settle:
-    # 100 warm-up steps (about 35 ms) then 100 timed steps
+    # 100 warm-up steps, the settle stretch, then 100 timed steps (about 30 ms)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gate_up", choices=["gate_up", "q_proj", "down_proj"])
     ap.add_argument("--variant", default="det-rtn", choices=sorted(VARIANTS),
                     help="rotation and rounding of the Wgrad operands")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="steps run back to back before timing, whatever --warmup is, until this many "
+                         "milliseconds have passed (the card's clocks settle under sustained load)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time each step after a 1 GiB write that flushes L2 and the memory-side "
+                         "cache; reports the median and minimum")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB copy kernel (counter calibration)")
@@ -454,8 +545,7 @@ def main() -> int:
         # both Wgrad operands (one rotation, one launch), then the GEMM
         i = counter[0]
         counter[0] += 1
-        sign_seed = 1000 + i if per_step_sign else 7
-        sr_dy, sr_x = (2 * i + 1, 2 * i + 2) if rnd == F.SR else (0, 0)
+        _, sign_seed, _, (sr_dy, sr_x) = step_settings(args.variant, i)
         if ev is not None:
             ev[0].record(stream)
         F.fp4_wgrad_quantize(dY, X, 32, had, sign_seed, rnd, sr_dy, sr_x, out=(dytq, dyts, xtq, xts))
@@ -468,15 +558,35 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    # settle: back-to-back steps for a fixed stretch of time, whatever
+    # --warmup is: the first tens of milliseconds of load run at other clocks
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize(dev)
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    from fp4_precision_gemms_amd import calib
+    span = calib.ClockSpan(dev, stream)
     # the timed steps: nothing but the two launches per step (an event record
-    # between launches costs about 3 % of the step)
+    # between launches costs about 3 % of the step); one clock-stamp kernel
+    # before and after, outside the events
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    span.begin()
     start.record(stream)
     for i in range(args.steps):
         step()
     stop.record(stream)
+    span.end()
     torch.cuda.synchronize(dev)
     ms_step = start.elapsed_time(stop) / args.steps
+    sclk = span.ghz()
+    last_timed = counter[0] - 1
+    timed = None
+    if not args.no_cpu_baseline:
+        timed = (last_timed, dytq.cpu().numpy(), dyts.cpu().numpy(), xtq.cpu().numpy(),
+                 xts.cpu().numpy(), dw.cpu().numpy())
     # per-launch durations: the same number of steps again, HIP events on the
     # launch stream around each launch
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -491,6 +601,40 @@ def main() -> int:
     flops = 2.0 * T * N * K
     gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
     q_gbs = (quant_bytes(T * N) + quant_bytes(T * K)) / (t_q * 1e-3) / 1e9
+    # the box's device-to-device copy rate (512 MiB each way), the practical
+    # ceiling of a read-once write-once kernel
+    csrc = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize(dev)
+    copy_gbs = 2.0 * csrc.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
+    flushed = None
+    if args.flush:
+        # each step after a 1 GiB write (evicts L2 and the 256 MB
+        # memory-side cache), events around the step only
+        fbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(args.steps):
+            fbuf.zero_()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(e)
+            torch.cuda.synchronize(dev)
+            times.append((e[0].elapsed_time(e[2]), e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])))
+        del fbuf
+        import statistics
+        flushed = {"steps": len(times), "flush_bytes": 1 << 30,
+                   "step_ms_median": statistics.median(t[0] for t in times),
+                   "step_ms_min": min(t[0] for t in times),
+                   "quant_ms_median": statistics.median(t[1] for t in times),
+                   "gemm_ms_median": statistics.median(t[2] for t in times),
+                   "gemm_ms_min": min(t[2] for t in times)}
     traffic = traffic_per_launch()
     out = {
         "metric": METRIC if (w.name, args.variant) == ("gate_up", "det-rtn") else
@@ -512,10 +656,17 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": "gemm_mx_tn (Wgrad)",
                      "achieved": gemm_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / MXFP4_PEAK_TFLOPS, "traffic": traffic},
+        "settle": {"steps": settle_steps, "ms": settle_ms,
+                   "what": "back-to-back steps before the timed ones, whatever --warmup is"},
+        "sclk_GHz_timed": sclk,
         "breakdown": {"quant_dY_X_ms": t_q, "gemm_ms": t_gemm,
                       "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
-                      "gemm_TFLOPs": gemm_tflops},
+                      "d2d_copy_GBps": copy_gbs, "quantizer_frac_copy": q_gbs / copy_gbs,
+                      "gemm_TFLOPs": gemm_tflops,
+                      "gemm_frac_of_peak_at_timed_sclk": gemm_tflops / (MXFP4_PEAK_TFLOPS * sclk / 2.4)},
     }
+    if flushed is not None:
+        out["flushed"] = flushed
     if not args.no_mfma_ceiling:
         from fp4_precision_gemms_amd import calib
         ceil = calib.mfma_ceiling(dev)
@@ -525,7 +676,7 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, dY_np, X_np, args.variant)
+        out["cpu_baseline"] = cpu_baseline(w, dY_np, X_np, args.variant, timed)
     print(json.dumps(out), flush=True)
     return 0
 

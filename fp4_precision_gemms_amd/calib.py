@@ -28,6 +28,8 @@ def lib() -> ctypes.CDLL:
         L.fp4_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p]
         L.fp4_calib_mfma.restype = ctypes.c_int
+        L.fp4_calib_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.fp4_calib_clock_stamp.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -69,3 +71,52 @@ def mfma_ceiling(device, iters: int = 20000, warmup: int = 20, launches: int = 1
             "what": "scaled FP4 MFMA 32x32x64 only, random E2M1 operands in registers, the Wgrad "
                     "GEMM's wave tile (7x2 accumulators, two fragment sets), one workgroup of 4 "
                     "waves per CU"}
+
+
+STAMPS = 32                  # workgroups per clock stamp (FP4_CALIB_STAMPS)
+
+
+def span_ghz(begin, end) -> float:
+    """Shader clock in GHz between two clock stamps (lists of [shader ticks,
+    reference ticks, XCD id, 0] records): each XCD's first record in `begin`
+    is paired with its first in `end`; the median ratio over the pairs.
+    NaN if no XCD appears in both."""
+    first = {}
+    for rec in begin:
+        first.setdefault(rec[2], rec)
+    ratios = []
+    for rec in end:
+        f = first.pop(rec[2], None)
+        if f is not None and rec[1] > f[1]:
+            ratios.append((rec[0] - f[0]) / (rec[1] - f[1]))
+    if not ratios:
+        return float("nan")
+    ratios.sort()
+    return ratios[len(ratios) // 2] * REFCLK_HZ / 1e9
+
+
+class ClockSpan:
+    """The average shader clock over the work enqueued on `stream` between
+    begin() and end(): a clock-stamp launch at each end, read per XCD (the
+    median over the XCDs both stamps reached)."""
+
+    def __init__(self, device, stream=None):
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        self.buf = torch.zeros((2, STAMPS, 4), dtype=torch.int64, device=device)
+
+    def _stamp(self, i):
+        st = lib().fp4_calib_clock_stamp(self.buf[i].data_ptr(), self.stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("fp4_calib_clock_stamp failed with status %d" % st)
+
+    def begin(self):
+        self._stamp(0)
+
+    def end(self):
+        self._stamp(1)
+
+    def ghz(self) -> float:
+        """Shader clock in GHz (synchronizes); NaN if no XCD was stamped twice."""
+        torch.cuda.synchronize(self.buf.device)
+        b = self.buf.cpu().tolist()
+        return span_ghz(b[0], b[1])

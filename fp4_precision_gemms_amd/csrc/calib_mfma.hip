@@ -91,3 +91,26 @@ extern "C" int fp4_calib_mfma(const void* src, int grid, int iters, float* out, 
                        (const v4i*)src, iters, out, clocks);
     return hipGetLastError() == hipSuccess ? 0 : 5;
 }
+
+namespace {
+// One record per workgroup: shader-clock counter, 100 MHz reference
+// counter, and the id of the XCD (accelerator complex die) it ran on -- the
+// shader-clock counters of different XCDs are not one clock, so a span is
+// read only between two records of the same XCD.
+__global__ void clock_stamp(uint64_t* out) {
+    if (threadIdx.x == 0) {
+        uint64_t* r = out + 4 * blockIdx.x;
+        r[0] = __builtin_amdgcn_s_memtime();
+        r[1] = __builtin_amdgcn_s_memrealtime();
+        r[2] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;   // HW_REG_XCC_ID[3:0]
+        r[3] = 0;
+    }
+}
+}  // namespace
+
+extern "C" int fp4_calib_clock_stamp(uint64_t* out, void* stream) {
+    if (!out) return 1;
+    if ((uintptr_t)out & 7) return 3;
+    hipLaunchKernelGGL(clock_stamp, dim3(FP4_CALIB_STAMPS), dim3(64), 0, (hipStream_t)stream, out);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}

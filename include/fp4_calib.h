@@ -53,6 +53,19 @@ double fp4_calib_mfma_flops(int grid, int iters);
  * enqueued. */
 int fp4_calib_mfma(const void* src, int grid, int iters, float* out, uint64_t* clocks, void* stream);
 
+/* Workgroups launched by one fp4_calib_clock_stamp call. */
+#define FP4_CALIB_STAMPS 32
+
+/* Enqueues FP4_CALIB_STAMPS one-wave workgroups on `stream`; workgroup i
+ * writes record i of `out` (device, FP4_CALIB_STAMPS * 4 uint64, 8-byte
+ * aligned): the shader clock counter, the 100 MHz reference counter, and the
+ * id of the XCD it ran on (0..7), then a zero.  Two stamps around a stretch
+ * of work on the same stream give the average shader clock over it, ticks /
+ * reference ticks * 100 MHz, from any pair of records of the same XCD (each
+ * XCD counts its own clock).  Returns 0 when enqueued, 1 for a null `out`,
+ * 3 if it is misaligned, 5 if the launch failed. */
+int fp4_calib_clock_stamp(uint64_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ def declared():
 
 def test_declared_symbols_exported(C):
     names = declared()
-    assert names == ["fp4_calib_mfma", "fp4_calib_mfma_flops", "fp4_calib_mfma_src_bytes"]
+    assert names == ["fp4_calib_clock_stamp", "fp4_calib_mfma", "fp4_calib_mfma_flops", "fp4_calib_mfma_src_bytes"]
     out = subprocess.check_output(["nm", "-D", "--defined-only", C.LIB_PATH], text=True)
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     assert set(names) <= exported
@@ -46,9 +46,28 @@ def test_argument_errors(C):
     L = C.lib()
     A = 0x10000
     assert L.fp4_calib_mfma(0, 1, 1, A, A, None) == 1
+    assert L.fp4_calib_clock_stamp(None, None) == 1
+    assert L.fp4_calib_clock_stamp(A + 4, None) == 3
     assert L.fp4_calib_mfma(A, 1, 1, 0, A, None) == 1
     assert L.fp4_calib_mfma(A, 0, 1, A, A, None) == 2
     assert L.fp4_calib_mfma(A, 65537, 1, A, A, None) == 2
     assert L.fp4_calib_mfma(A, 1, 0, A, A, None) == 2
     assert L.fp4_calib_mfma(A, 1, (1 << 24) + 1, A, A, None) == 2
     assert L.fp4_calib_mfma(A + 8, 1, 1, A, A, None) == 3
+
+
+def test_span_ghz_pairs_records_of_one_xcd():
+    from fp4_precision_gemms_amd.calib import span_ghz
+    # XCD 0 ran at 2.0 GHz, XCD 1 at 1.5 GHz (own counter origins), XCD 2
+    # only in the second stamp: the median of the two pairs
+    begin = [[1000, 50, 0, 0], [9_000_000, 50, 1, 0], [1001, 51, 0, 0]]
+    end = [[9_000_000 + 15 * 100, 150, 1, 0], [1000 + 20 * 100, 150, 0, 0], [7, 150, 2, 0]]
+    assert abs(span_ghz(begin, end) - 2.0) < 1e-12        # upper median of [1.5, 2.0]
+    assert abs(span_ghz(begin[:1], end) - 2.0) < 1e-12
+    assert span_ghz(begin[:1], end[:1]) != span_ghz(begin[:1], end[:1])      # NaN: no common XCD
+
+
+def test_stamp_count_matches_header():
+    from fp4_precision_gemms_amd.calib import STAMPS
+    m = re.search(r"#define FP4_CALIB_STAMPS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == STAMPS
