@@ -213,6 +213,8 @@ def gemm_rows(aq, as_, bq, bs, m0=0, m1=None):
     N = bq.shape[0]
     assert bq.shape[1] * 2 == K and as_.shape == (M, K // 32) and bs.shape == (N, K // 32)
     m1 = M if m1 is None else m1
+    if not 0 <= m0 <= m1 <= M:
+        raise ValueError("rows %d..%d outside 0..%d" % (m0, m1, M))
     c = np.zeros((m1 - m0, N), dtype=np.float64)
     s = np.zeros((m1 - m0, N), dtype=np.float64)
     lib().oracle_gemm_mx_rows(aq, as_, bq, bs, M, N, K, m0, m1, c, s)
@@ -225,6 +227,9 @@ def gemm_entries(aq, as_, bq, bs, mi, ni):
     K = aq.shape[1] * 2
     mi = np.ascontiguousarray(mi, np.int64)
     ni = np.ascontiguousarray(ni, np.int64)
+    if mi.shape != ni.shape or (mi.size and (mi.min() < 0 or mi.max() >= aq.shape[0] or
+                                            ni.min() < 0 or ni.max() >= bq.shape[0])):
+        raise ValueError("entry indices outside the product")
     c = np.zeros(mi.shape[0], dtype=np.float64)
     s = np.zeros(mi.shape[0], dtype=np.float64)
     lib().oracle_gemm_mx_entries(aq, as_, bq, bs, K, mi, ni, mi.shape[0], c, s)

@@ -163,7 +163,9 @@ FULL = [("gate_up", "dY", O.AXIS_ROWS, O.HAD_DET, O.RND_RTN),
 @pytest.mark.slow
 @pytest.mark.parametrize("wname,tname,axis,had,rnd", FULL)
 def test_quant_parity_full_size_sampled_rows(wname, tname, axis, had, rnd):
-    """Full Llama-3.1-8B shapes, the launch the benchmark times; the oracle
+    """Full Llama-3.1-8B shapes through fp4_hadamard_quantize, the
+    single-tensor entry point (the benchmark times fp4_wgrad_quantize, the
+    pair launch, which test_gpu_full_size.py checks whole); the oracle
     recomputes three ranges of 64 logical rows (first, middle, last)."""
     w = W.WORKLOADS[wname]
     bits = W.tensor(w, tname)

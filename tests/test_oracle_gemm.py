@@ -146,3 +146,19 @@ def test_nan_scale_propagates():
     bs = np.array([[127], [127]], np.uint8)
     c, _ = O.gemm_rows(aq, as_, bq, bs)
     assert np.isnan(c).all()
+
+
+def test_row_and_entry_ranges_checked():
+    """Rows or entries outside the product are refused before the C code
+    runs (it would read past the operands)."""
+    rng = np.random.default_rng(0)
+    aq = rng.integers(0, 256, (4, 16), dtype=np.uint8)
+    as_ = np.full((4, 1), 127, dtype=np.uint8)
+    for m0, m1 in ((0, 5), (-1, 2), (3, 2)):
+        with pytest.raises(ValueError):
+            O.gemm_rows(aq, as_, aq, as_, m0, m1)
+    for mi, ni in (([4], [0]), ([0], [-1]), ([0, 1], [0])):
+        with pytest.raises(ValueError):
+            O.gemm_entries(aq, as_, aq, as_, np.array(mi), np.array(ni))
+    c, s = O.gemm_rows(aq, as_, aq, as_, 4, 4)
+    assert c.shape == (0, 4)
