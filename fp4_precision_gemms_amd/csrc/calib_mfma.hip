@@ -87,9 +87,11 @@ extern "C" int fp4_calib_mfma(const void* src, int grid, int iters, float* out, 
     if (!src || !out || !clocks) return 1;
     if (grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 24)) return 2;
     if (((uintptr_t)src | (uintptr_t)out | (uintptr_t)clocks) & 15) return 3;
-    hipLaunchKernelGGL(mfma_loop, dim3((unsigned)grid), dim3(64 * kWaves), 0, (hipStream_t)stream,
-                       (const v4i*)src, iters, out, clocks);
-    return hipGetLastError() == hipSuccess ? 0 : 5;
+    const v4i* s = (const v4i*)src;
+    void* args[] = {(void*)&s, (void*)&iters, (void*)&out, (void*)&clocks};
+    // the status of this launch alone (not an earlier call's, as hipGetLastError)
+    return hipLaunchKernel((const void*)mfma_loop, dim3((unsigned)grid), dim3(64 * kWaves), args, 0,
+                           (hipStream_t)stream) == hipSuccess ? 0 : 5;
 }
 
 namespace {
@@ -111,6 +113,7 @@ __global__ void clock_stamp(uint64_t* out) {
 extern "C" int fp4_calib_clock_stamp(uint64_t* out, void* stream) {
     if (!out) return 1;
     if ((uintptr_t)out & 7) return 3;
-    hipLaunchKernelGGL(clock_stamp, dim3(FP4_CALIB_STAMPS), dim3(64), 0, (hipStream_t)stream, out);
-    return hipGetLastError() == hipSuccess ? 0 : 5;
+    void* args[] = {(void*)&out};
+    return hipLaunchKernel((const void*)clock_stamp, dim3(FP4_CALIB_STAMPS), dim3(64), args, 0,
+                           (hipStream_t)stream) == hipSuccess ? 0 : 5;
 }

@@ -5,7 +5,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace fp4dev {
+
+// Launches kernel k with the arguments converted to its parameter types and
+// returns the status of this launch alone (hipLaunchKernel), not an error
+// left over from earlier runtime calls as hipGetLastError would.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... a) {
+    static_assert(sizeof...(P) == sizeof...(A), "argument count");
+    std::tuple<P...> v(static_cast<P>(a)...);
+    return std::apply(
+        [&](auto&... e) {
+            void* args[] = {(void*)&e..., nullptr};
+            return hipLaunchKernel((const void*)k, grid, block, args, 0, st);
+        },
+        v);
+}
 
 // MXFP4 quantization of bf16 x[rows, cols] along axis 0 (cols) or 1 (rows).
 hipError_t launch_quant_mx(const void* x, int64_t rows, int64_t cols, int axis, int had_n, int had,

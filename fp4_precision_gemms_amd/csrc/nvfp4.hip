@@ -345,29 +345,27 @@ hipError_t launch_nv_had(const void* x, int64_t rows, int64_t cols, uint32_t sw,
     const float* amax_p = amax_in;
     if (!amax_p) {
         uint32_t* ws = (uint32_t*)workspace;
-        hipLaunchKernelGGL(nv_clear, dim3(1), dim3(64), 0, st, ws);
+        hipError_t e = launch(&nv_clear, dim3(1), dim3(64), st, ws);
+        if (e != hipSuccess) return e;
         int64_t blocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
         if (blocks > kAmaxBlocks) blocks = kAmaxBlocks;
-        hipLaunchKernelGGL((nv_amax<HAD>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                           (const uint4*)x, nchunks, sw, ws);
+        e = launch(&nv_amax<HAD>, dim3((unsigned)blocks), dim3(kThreads), st, (const uint4*)x, nchunks,
+                   sw, ws);
+        if (e != hipSuccess) return e;
         amax_p = (const float*)ws;
     }
     const int64_t qblocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
     if (mode == 1) {
         const int64_t nblocks = nchunks / 2, per_wg = (int64_t)(kThreads / 64) * 256;
-        hipLaunchKernelGGL((nv_quant_renorm<HAD>), dim3((unsigned)((nblocks + per_wg - 1) / per_wg)),
-                           dim3(kThreads), 0, st, (const uint4*)x, nblocks, sw, amax_p, sr_seed,
-                           (uint2*)codes, scales, tensor_scale);
-    } else if (mode == 2) {
-        hipLaunchKernelGGL((nv_quant<HAD, 2>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
-                           (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
-                           tensor_scale);
-    } else {
-        hipLaunchKernelGGL((nv_quant<HAD, 0>), dim3((unsigned)qblocks), dim3(kThreads), 0, st,
-                           (const uint4*)x, nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales,
-                           tensor_scale);
+        return launch(&nv_quant_renorm<HAD>, dim3((unsigned)((nblocks + per_wg - 1) / per_wg)),
+                      dim3(kThreads), st, (const uint4*)x, nblocks, sw, amax_p, sr_seed, (uint2*)codes,
+                      scales, tensor_scale);
     }
-    return hipGetLastError();
+    if (mode == 2)
+        return launch(&nv_quant<HAD, 2>, dim3((unsigned)qblocks), dim3(kThreads), st, (const uint4*)x,
+                      nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales, tensor_scale);
+    return launch(&nv_quant<HAD, 0>, dim3((unsigned)qblocks), dim3(kThreads), st, (const uint4*)x,
+                  nchunks, sw, amax_p, sr_seed, (uint32_t*)codes, scales, tensor_scale);
 }
 
 }  // namespace

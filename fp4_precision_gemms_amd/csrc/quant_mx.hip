@@ -564,9 +564,8 @@ template <int HADN, bool SR>
 hipError_t launch_cols(const void* x, int64_t rows, int64_t cols, uint32_t sign_word, float norm,
                        uint64_t sr_seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
     const int64_t blocks = ((cols + 255) / 256) * ((rows + 31) / 32);
-    hipLaunchKernelGGL((quant_mx_along_cols<HADN, SR>), dim3((unsigned)blocks), dim3(kColsThreads), 0, st,
-                       (const uint16_t*)x, rows, cols, sign_word, norm, sr_seed, codes, scales);
-    return hipGetLastError();
+    return launch(&quant_mx_along_cols<HADN, SR>, dim3((unsigned)blocks), dim3(kColsThreads), st,
+                  (const uint16_t*)x, rows, cols, sign_word, norm, sr_seed, codes, scales);
 }
 
 template <int CPL, int HADN, bool SR>
@@ -576,10 +575,9 @@ hipError_t launch_rows(const void* x, int64_t rows, int64_t cols, uint32_t sign_
     const int64_t nrb = rows / 32;
     const int64_t gx = (cols + 64 * CPL - 1) / (64 * CPL);
     const int64_t gy = (nrb + kRowsWaves * RBW - 1) / (kRowsWaves * RBW);
-    hipLaunchKernelGGL((quant_mx_along_rows<CPL, HADN, SR, RBW>), dim3((unsigned)gx, (unsigned)gy),
-                       dim3(64 * kRowsWaves), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
-                       sr_seed, codes, scales);
-    return hipGetLastError();
+    return launch(&quant_mx_along_rows<CPL, HADN, SR, RBW>, dim3((unsigned)gx, (unsigned)gy),
+                  dim3(64 * kRowsWaves), st, (const uint16_t*)x, rows, cols, sign_word, norm, sr_seed,
+                  codes, scales);
 }
 
 // 32-row blocks per workgroup of the LDS kernel: two (32 KB of LDS) keeps
@@ -596,11 +594,10 @@ hipError_t dispatch_rows_cpl(const void* x, int64_t rows, int64_t cols, uint32_t
         const int64_t gx = (cols + kTileCols - 1) / kTileCols;
         constexpr int TB = kRowsLdsBlocks;
         const int64_t gy = (rows / 32 + TB - 1) / TB;
-        hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, -1>), dim3((unsigned)gx, (unsigned)gy),
-                           dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
-                           sr_seed, codes, scales, 0u, 1.0f, (uint64_t)0, (uint8_t*)nullptr,
-                           (uint8_t*)nullptr, RowsLdsSecond{});
-        return hipGetLastError();
+        return launch(&quant_mx_along_rows_lds<HADN, SR, TB, -1>, dim3((unsigned)gx, (unsigned)gy),
+                      dim3(kTileCols), st, (const uint16_t*)x, rows, cols, sign_word, norm, sr_seed,
+                      codes, scales, 0u, 1.0f, (uint64_t)0, (uint8_t*)nullptr, (uint8_t*)nullptr,
+                      RowsLdsSecond{});
     }
     if (cols % 4 == 0) return launch_rows<4, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
     if (cols % 2 == 0) return launch_rows<2, HADN, SR>(x, rows, cols, sign_word, norm, sr_seed, codes, scales, st);
@@ -629,11 +626,9 @@ hipError_t launch_dual(const void* x, int64_t rows, int64_t cols, uint32_t sign_
     constexpr int TB = kRowsLdsBlocks;
     const int64_t gx = (cols + kTileCols - 1) / kTileCols;
     const int64_t gy = (rows / 32 + TB - 1) / TB;
-    hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, HADN_C>), dim3((unsigned)gx, (unsigned)gy),
-                       dim3(kTileCols), 0, st, (const uint16_t*)x, rows, cols, sign_word, norm,
-                       sr_seed, codes, scales, sign_word_c, norm_c, sr_seed_c, codes_c, scales_c,
-                       RowsLdsSecond{});
-    return hipGetLastError();
+    return launch(&quant_mx_along_rows_lds<HADN, SR, TB, HADN_C>, dim3((unsigned)gx, (unsigned)gy),
+                  dim3(kTileCols), st, (const uint16_t*)x, rows, cols, sign_word, norm, sr_seed, codes,
+                  scales, sign_word_c, norm_c, sr_seed_c, codes_c, scales_c, RowsLdsSecond{});
 }
 
 template <int HADN, bool SR>
@@ -661,10 +656,9 @@ hipError_t launch_pair(const void* a, int64_t rows, int64_t n1, const void* b, i
     const int64_t gy = (rows / 32 + TB - 1) / TB;
     const int64_t gx1 = (n1 + kTileCols - 1) / kTileCols, gx2 = (n2 + kTileCols - 1) / kTileCols;
     const RowsLdsSecond second{(const uint16_t*)b, n2, sr_b, qb, sb, gx1 * gy, gx1, gx2};
-    hipLaunchKernelGGL((quant_mx_along_rows_lds<HADN, SR, TB, -1>), dim3((unsigned)((gx1 + gx2) * gy)),
-                       dim3(kTileCols), 0, st, (const uint16_t*)a, rows, n1, sign_word, norm, sr_a,
-                       qa, sa, 0u, 1.0f, (uint64_t)0, (uint8_t*)nullptr, (uint8_t*)nullptr, second);
-    return hipGetLastError();
+    return launch(&quant_mx_along_rows_lds<HADN, SR, TB, -1>, dim3((unsigned)((gx1 + gx2) * gy)),
+                  dim3(kTileCols), st, (const uint16_t*)a, rows, n1, sign_word, norm, sr_a, qa, sa, 0u,
+                  1.0f, (uint64_t)0, (uint8_t*)nullptr, (uint8_t*)nullptr, second);
 }
 
 // Rotation size and the binary32 factor fl(1/sqrt(n)) of a (had, had_n) pair.
