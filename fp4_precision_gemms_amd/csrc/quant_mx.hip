@@ -314,9 +314,15 @@ __global__ __launch_bounds__(64 * kRowsWaves) void quant_mx_along_rows(
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Wave-wide DMA: each lane's 16 bytes at voff of the buffer go to LDS at
-// lds_dst + 16 * lane (lds_dst wave-uniform).
+// lds_dst + 16 * lane (lds_dst wave-uniform).  The input is read once, so the
+// load is marked non-temporal (cache policy bit 1, NT).  Measured on the
+// Wgrad pair dY[8192x14336] + X[8192x4096]: 64 us instead of 70 us back to
+// back, and the whole Llama-3.1-8B gate/up linear layer 5 % faster.  Marking
+// the code stores non-temporal too speeds the quantizer alike but slows the
+// GEMM that reads the codes next (they then miss the caches); the same hint
+// on the along-cols and NVFP4 kernels' plain loads measured no gain.
 __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_dst, 16, voff, 0, 0, 2);
 }
 
 constexpr int kTileCols = 256;           // columns per block, one per thread
