@@ -72,9 +72,12 @@ def quant_bytes(elems: int) -> float:
     return elems * (2.0 + 0.5 + 1.0 / 32.0)
 
 
-def traffic_per_launch():
-    """HBM bytes per GEMM launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_per_launch(workload="gate_up"):
+    """HBM bytes per GEMM launch from the committed counter summary (taken
+    on the gate/up Wgrad), if it was taken on the current kernel source and
+    `workload` is that shape; else None."""
+    if workload != "gate_up":
+        return None
     try:
         with open(COUNTERS) as f:
             rec = json.load(f)
@@ -635,7 +638,7 @@ def main() -> int:
                    "quant_ms_median": statistics.median(t[1] for t in times),
                    "gemm_ms_median": statistics.median(t[2] for t in times),
                    "gemm_ms_min": min(t[2] for t in times)}
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(w.name)
     out = {
         "metric": METRIC if (w.name, args.variant) == ("gate_up", "det-rtn") else
                   "MXFP4 Wgrad TFLOPS incl. rotation+quantize (%dx%dx%d, %s)" % (T, N, K, args.variant),
@@ -658,7 +661,12 @@ def main() -> int:
                      "frac": gemm_tflops / MXFP4_PEAK_TFLOPS, "traffic": traffic},
         "settle": {"steps": settle_steps, "ms": settle_ms,
                    "what": "back-to-back steps before the timed ones, whatever --warmup is"},
-        "sclk_GHz_timed": sclk,
+        "timed_clock": {"sclk_GHz": sclk,
+                        "what": "shader clock counter (s_memtime) against the 100 MHz reference "
+                                "(s_memrealtime) between clock-stamp launches on either side of the "
+                                "timed steps, median over the XCDs; under the power limit the matrix "
+                                "cores' rate is not proportional to it (measured: equal kernel times "
+                                "at rates 13 % apart)"},
         "breakdown": {"quant_dY_X_ms": t_q, "gemm_ms": t_gemm,
                       "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
                       "d2d_copy_GBps": copy_gbs, "quantizer_frac_copy": q_gbs / copy_gbs,
