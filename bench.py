@@ -18,11 +18,12 @@ are synthetic bf16 tensors resident in HBM before timing starts.
     python bench.py --autograd [--workload W]          (MXFP4LinearFunction forward + backward, bf16)
     python bench.py --mfma-ceiling                     (only the MFMA-rate measurement aid)
 
-Procedure: W warm-up steps, then back-to-back steps for --settle-ms
-milliseconds whatever W is (reported as "settle": the card's clocks take
-tens of milliseconds of load to settle), then the K timed steps holding
+Procedure: W warm-up steps and a 10-step probe, a host synchronization, then
+with no host synchronization in between (the card must not idle before the
+measured windows): back-to-back steps for --settle-ms of GPU time whatever W
+is (reported as "settle"), the K timed steps between two events holding
 nothing but their launches, with a clock-stamp kernel on either side
-(sclk_GHz_timed: the average shader clock over them).  Prints one JSON line.
+(timed_clock), and the event pass.  Prints one JSON line.
 `value` is Wgrad TFLOP/s including quantization (2 T N K flops per step);
 the roofline object describes the dominant kernel (the GEMM) from HIP
 events around each launch over a second pass of K steps; breakdown holds
@@ -87,6 +88,34 @@ def traffic_per_launch(workload="gate_up"):
     except (OSError, ValueError, KeyError):
         pass
     return None
+
+
+def gapless_window(torch, dev, step, steps, settle_ms, after=None):
+    """Times `steps` calls of `step` (warm-up already done): a 10-call probe
+    of the call's duration and a host synchronization, then -- enqueued with
+    no host synchronization between them, so the card does not idle before
+    the window -- settle calls for about `settle_ms` of GPU time, the timed
+    calls between two events on the current stream, and `after()` (another
+    measured pass) if given; then a synchronization.  Returns (ms per timed
+    call, settle calls, settle ms)."""
+    t = time.perf_counter()
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize(dev)
+    per = (time.perf_counter() - t) / 10
+    n = int(settle_ms * 1e-3 / per) if settle_ms > 0 else 0
+    s0, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    s0.record()
+    for _ in range(n):
+        step()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    if after is not None:
+        after()
+    torch.cuda.synchronize(dev)
+    return e0.elapsed_time(e1) / steps, n, s0.elapsed_time(e0)
 
 
 COPY_BYTES = 256 << 20           # the calibration copy reads and writes this many bytes
@@ -295,13 +324,7 @@ def nvfp4_bench(args) -> int:
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize(dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize(dev)
-        return e0.elapsed_time(e1) / args.steps
+        return gapless_window(torch, dev, fn, args.steps, args.settle_ms)[0]
 
     el = rows * cols
     t2 = timed(lambda: F.nvfp4_quantize(x, F.HAD_SIGNED, 7, F.NV_RENORM_SR, 11, codes=codes, scales=scales,
@@ -368,22 +391,19 @@ def layer_bench(args) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1) / args.steps
-    # per-launch times, in a second timed pass with events around each launch
+    # per-launch times, in a second pass with events around each launch,
+    # right behind the timed steps
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in launches] for _ in range(args.steps)]
-    for i in range(args.steps):
-        for (a, b), (_, fn) in zip(ev[i], launches):
-            a.record()
-            fn()
-            b.record()
-    torch.cuda.synchronize(dev)
+
+    def event_pass():
+        for i in range(args.steps):
+            for (a, b), (_, fn) in zip(ev[i], launches):
+                a.record()
+                fn()
+                b.record()
+
+    ms, settle_steps, settle_ms = gapless_window(torch, dev, step, args.steps, args.settle_ms, event_pass)
     per = {name: 1e3 * sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)) / args.steps
            for j, (name, _) in enumerate(launches)}
     flop = 2.0 * T * N * K
@@ -409,6 +429,7 @@ def layer_bench(args) -> int:
                      "achieved": flop / (gemm_us * 1e-6) / 1e12, "peak": MXFP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flop / (gemm_us * 1e-6) / 1e12 / MXFP4_PEAK_TFLOPS,
                      "traffic": None},
+        "settle": {"steps": settle_steps, "ms": settle_ms},
         "breakdown": breakdown}), flush=True)
     return 0
 
@@ -443,13 +464,7 @@ def autograd_bench(args) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, settle_steps, settle_ms = gapless_window(torch, dev, step, args.steps, args.settle_ms)
     flop = 3 * 2.0 * T * N * K
     print(json.dumps({
         "metric": "MXFP4 linear layer training step TFLOP/s (autograd forward + backward, %dx%dx%d)" % (T, N, K),
@@ -458,7 +473,8 @@ def autograd_bench(args) -> int:
         "data": "synthetic",
         "config": {"workload": "%s MXFP4LinearFunction forward + backward" % w.name, "T": T, "N": N, "K": K,
                    "hadamard": "deterministic-32 on the Wgrad operands", "rounding": "rtn",
-                   "outputs": "bf16 Y, dX, dW"}}), flush=True)
+                   "outputs": "bf16 Y, dX, dW"},
+        "settle": {"steps": settle_steps, "ms": settle_ms}}), flush=True)
     return 0
 
 
@@ -561,41 +577,57 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    # settle: back-to-back steps for a fixed stretch of time, whatever
-    # --warmup is: the first tens of milliseconds of load run at other clocks
-    settle_steps, t_settle = 0, time.perf_counter()
-    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        for _ in range(20):
-            step()
-        settle_steps += 20
-        torch.cuda.synchronize(dev)
-    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    # settle: back-to-back steps for a fixed stretch of GPU time, whatever
+    # --warmup is (the first tens of milliseconds of load run at other
+    # clocks).  The step count comes from a short probe; the settle steps,
+    # the timed steps and the event pass are then enqueued with no host
+    # synchronization between them, so the card never idles before or
+    # between the measured windows (after even a short idle the next few
+    # milliseconds run slower, which a 20-step window would measure).
+    t_probe = time.perf_counter()
+    for _ in range(10):
+        step()
+    torch.cuda.synchronize(dev)
+    per_step_s = (time.perf_counter() - t_probe) / 10
+    settle_steps = int(args.settle_ms * 1e-3 / per_step_s) if args.settle_ms > 0 else 0
     from fp4_precision_gemms_amd import calib
     span = calib.ClockSpan(dev, stream)
+    # everything the measured sequence uses is allocated before it starts
+    snap = None
+    if not args.no_cpu_baseline:
+        snap = [torch.empty_like(t) for t in (dytq, dyts, xtq, xts, dw)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    s0 = torch.cuda.Event(enable_timing=True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(settle_steps):
+        step()
     # the timed steps: nothing but the two launches per step (an event record
     # between launches costs about 3 % of the step); one clock-stamp kernel
     # before and after, outside the events
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     span.begin()
     start.record(stream)
     for i in range(args.steps):
         step()
     stop.record(stream)
     span.end()
-    torch.cuda.synchronize(dev)
-    ms_step = start.elapsed_time(stop) / args.steps
-    sclk = span.ghz()
     last_timed = counter[0] - 1
-    timed = None
-    if not args.no_cpu_baseline:
-        timed = (last_timed, dytq.cpu().numpy(), dyts.cpu().numpy(), xtq.cpu().numpy(),
-                 xts.cpu().numpy(), dw.cpu().numpy())
+    # the last timed step's outputs, kept on the device for the parity check
+    if snap is not None:
+        for d, t in zip(snap, (dytq, dyts, xtq, xts, dw)):
+            d.copy_(t)
     # per-launch durations: the same number of steps again, HIP events on the
     # launch stream around each launch
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize(dev)
+    settle_ms = s0.elapsed_time(start)
+    ms_step = start.elapsed_time(stop) / args.steps
+    sclk = span.ghz()
+    timed = None
+    if snap is not None:
+        timed = (last_timed, *(t.cpu().numpy() for t in snap))
+        del snap
 
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
@@ -660,7 +692,8 @@ def main() -> int:
                      "achieved": gemm_tflops, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / MXFP4_PEAK_TFLOPS, "traffic": traffic},
         "settle": {"steps": settle_steps, "ms": settle_ms,
-                   "what": "back-to-back steps before the timed ones, whatever --warmup is"},
+                   "what": "back-to-back steps right before the timed ones (GPU time), whatever --warmup is; "
+                           "settle, timed steps and event pass run with no host synchronization between them"},
         "timed_clock": {"sclk_GHz": sclk,
                         "what": "shader clock counter (s_memtime) against the 100 MHz reference "
                                 "(s_memrealtime) between clock-stamp launches on either side of the "
