@@ -500,7 +500,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         __syncthreads();                                // all fragment reads of the tile are done
         const int64_t em0 = m0, en0 = n0;               // the tile the epilogue writes
         const bool vec_store = (N % 4) == 0;
-        const bool full_tile = vec_store && em0 + BM <= M && en0 + kBN <= N;   // workgroup-uniform
+        // workgroup-uniform; constant on the fast path, whose tiles are all
+        // full: the epilogue then has no partial-tile branch, whose zero-store
+        // path made the compiler wait for most of these stores before the
+        // next tile's first fragment moves
+        const bool full_tile = FAST || (vec_store && em0 + BM <= M && en0 + kBN <= N);
         early = false;
         if constexpr (!KTAIL && !ACC) {
             // The next tile's first stages go out now, into slots 0..2 (this
