@@ -27,7 +27,8 @@ nothing but their launches, with a clock-stamp kernel on either side
 `value` is Wgrad TFLOP/s including quantization (2 T N K flops per step);
 the roofline object describes the dominant kernel (the GEMM) from HIP
 events around each launch over a second pass of K steps; breakdown holds
-both kernels and the card's device-to-device copy rate; --flush adds a pass
+both kernels, the quantizer's launches alone (K back to back, after 50 ms of
+them) and the card's device-to-device copy rate; --flush adds a pass
 with a 1 GiB write before each step (cold L2 and memory-side cache, median
 and minimum); cpu_baseline times the plain CPU oracle on a bounded sample of
 the same workload and checks the last timed step's outputs against it
@@ -635,7 +636,20 @@ def main() -> int:
     t_q, t_gemm = avg(0, 1), avg(1, 2)
     flops = 2.0 * T * N * K
     gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
-    q_gbs = (quant_bytes(T * N) + quant_bytes(T * K)) / (t_q * 1e-3) / 1e9
+    q_bytes = quant_bytes(T * N) + quant_bytes(T * K)
+    q_gbs = q_bytes / (t_q * 1e-3) / 1e9
+
+    # the quantizer alone: the same launch back to back, no GEMM between
+    # (against its time inside the step, where it follows the GEMM)
+    _, q_sign, _, (q_sr_dy, q_sr_x) = step_settings(args.variant, 0)
+
+    def qstep():
+        F.fp4_wgrad_quantize(dY, X, 32, had, q_sign, rnd, q_sr_dy, q_sr_x, out=(dytq, dyts, xtq, xts))
+
+    for _ in range(10):
+        qstep()
+    t_q_alone = gapless_window(torch, dev, qstep, args.steps, 50.0)[0]
+    q_alone_gbs = q_bytes / (t_q_alone * 1e-3) / 1e9
     # the box's device-to-device copy rate (512 MiB each way), the practical
     # ceiling of a read-once write-once kernel
     csrc = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -702,6 +716,8 @@ def main() -> int:
                                 "at rates 13 % apart)"},
         "breakdown": {"quant_dY_X_ms": t_q, "gemm_ms": t_gemm,
                       "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
+                      "quantizer_alone_ms": t_q_alone, "quantizer_alone_GBps": q_alone_gbs,
+                      "quantizer_alone_frac_hbm": q_alone_gbs / HBM_PEAK_GBS,
                       "d2d_copy_GBps": copy_gbs, "quantizer_frac_copy": q_gbs / copy_gbs,
                       "gemm_TFLOPs": gemm_tflops,
                       "gemm_frac_of_peak_at_timed_sclk": gemm_tflops / (MXFP4_PEAK_TFLOPS * sclk / 2.4)},
