@@ -74,14 +74,14 @@ def quant_bytes(elems: int) -> float:
     return elems * (2.0 + 0.5 + 1.0 / 32.0)
 
 
-def traffic_per_launch(workload="gate_up"):
+def traffic_per_launch(workload="gate_up", path=None):
     """HBM bytes per GEMM launch from the committed counter summary (taken
-    on the gate/up Wgrad), if it was taken on the current kernel source and
-    `workload` is that shape; else None."""
+    on the gate/up Wgrad; `path` defaults to it), if it was taken on the
+    current kernel source and `workload` is that shape; else None."""
     if workload != "gate_up":
         return None
     try:
-        with open(COUNTERS) as f:
+        with open(path or COUNTERS) as f:
             rec = json.load(f)
         src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
         if rec.get("gemm_source_sha256") == src:
@@ -134,12 +134,16 @@ def copy_calibration(torch, dev):
     torch.cuda.synchronize(dev)
 
 
-def counter_summary(fetch_dir, write_dir):
+def counter_summary(fetch_dir, write_dir, out=None):
     """Reads the rocprofv3 counter CSVs of two runs of
         rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run --
-            python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration
-    and writes the calibrated HBM traffic per GEMM launch next to the kernel
-    trace summaries (JSON for bench.py, Markdown for readers)."""
+            python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline
+                --copy-calibration --no-mfma-ceiling
+    and writes the calibrated HBM traffic per GEMM launch, with the GEMM
+    source's hash, to `out` (default: the summary bench.py reads beside the
+    kernel traces; the Markdown next to it is written by hand).  The copy
+    kernel's readings (COPY_BYTES each way) give each counter's bytes per
+    counted KiB."""
     import csv
     import glob
 
@@ -182,7 +186,7 @@ def counter_summary(fetch_dir, write_dir):
            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
            "hbm_bytes_per_launch": rd + wr,
            "gemm_source_sha256": hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()}
-    with open(COUNTERS, "w") as f:
+    with open(out or COUNTERS, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
     return 0
