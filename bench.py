@@ -733,6 +733,14 @@ def main() -> int:
         ceil = calib.mfma_ceiling(dev)
         ceil["frac_of_peak"] = ceil["value"] / MXFP4_PEAK_TFLOPS
         ceil["gemm_frac_of_ceiling"] = gemm_tflops / ceil["value"]
+        # the same loop on this product's own quantized operands (fragments of
+        # dY^T and X^T as the GEMM reads them): the matrix cores' power, hence
+        # their rate under the power limit, depends on the operand bits
+        own = calib.mfma_ceiling(dev, operands=(dytq, xtq))
+        ceil["on_operands"] = {"value": own["value"], "sclk_GHz": own["sclk_GHz"],
+                               "frac_of_peak": own["value"] / MXFP4_PEAK_TFLOPS,
+                               "gemm_frac_of_ceiling": gemm_tflops / own["value"],
+                               "what": own["what"]}
         out["mfma_ceiling"] = ceil
     if args.copy_calibration:
         copy_calibration(torch, dev)

@@ -1,7 +1,8 @@
 """Binding of libfp4calib.so (include/fp4_calib.h): the scaled FP4 MFMA rate
-the card sustains on random operands under its power limit, with the shader
-clock it ran at.  A measurement aid for the GEMM's roofline, not part of the
-quantized-GEMM path."""
+the card sustains under its power limit, on random operands or on a real
+product's own quantized operands, with the shader clock it ran at.  A
+measurement aid for the GEMM's roofline, not part of the quantized-GEMM
+path."""
 from __future__ import annotations
 
 import ctypes
@@ -34,17 +35,44 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def mfma_ceiling(device, iters: int = 20000, warmup: int = 20, launches: int = 10, seed: int = 0) -> dict:
+def operand_fragments(a_codes, b_codes, waves: int):
+    """The MFMA-only loop's operands taken from real MXFP4 operands in the
+    library's 32-row tiled layout (whose consecutive 1 KB pieces are the
+    32x32x64 MFMA operands in lane order): wave w's A fragments are pieces
+    14 w .. 14 w + 13 of `a_codes` and its B fragments pieces 4 w .. 4 w + 3
+    of `b_codes` (modulo their piece counts), in the loop's fragment order."""
+    fa, fb = a_codes.reshape(-1, 1024), b_codes.reshape(-1, 1024)
+    dev = a_codes.device
+    w = torch.arange(waves, device=dev)
+    ia = (w[:, None, None] * 14 + torch.arange(2, device=dev)[None, :, None] * 7 +
+          torch.arange(7, device=dev)[None, None, :]) % fa.shape[0]
+    ib = (w[:, None, None] * 4 + torch.arange(2, device=dev)[None, :, None] * 2 +
+          torch.arange(2, device=dev)[None, None, :]) % fb.shape[0]
+    # [waves, set, 7 A + 2 B, 1024]
+    return torch.cat([fa[ia], fb[ib]], dim=2).reshape(-1).contiguous()
+
+
+def mfma_ceiling(device, iters: int = 20000, warmup: int = 20, launches: int = 10, seed: int = 0,
+                 operands=None) -> dict:
     """Runs the MFMA-only loop on one workgroup per CU: `warmup` launches to
     let the clocks settle, then `launches` timed ones (HIP events on the
-    launch stream).  Returns TFLOP/s and the median shader clock over all
-    waves of the timed launches."""
+    launch stream).  Operands: random E2M1 bytes, or `operands` = (A codes,
+    B codes) of a real product (see operand_fragments) -- the matrix cores'
+    power, and so their rate under the power limit, depends on the data.
+    Returns TFLOP/s and the median shader clock over all waves of the timed
+    launches."""
     L = lib()
     grid = torch.cuda.get_device_properties(device).multi_processor_count
-    g = torch.Generator(device=device)
-    g.manual_seed(seed)
-    src = torch.randint(0, 256, (L.fp4_calib_mfma_src_bytes(grid),), dtype=torch.uint8, device=device,
-                        generator=g)
+    if operands is None:
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        src = torch.randint(0, 256, (L.fp4_calib_mfma_src_bytes(grid),), dtype=torch.uint8,
+                            device=device, generator=g)
+    else:
+        src = operand_fragments(operands[0], operands[1], grid * 4)
+        if src.numel() != L.fp4_calib_mfma_src_bytes(grid):
+            raise ValueError("operand fragments: %d bytes, the loop takes %d"
+                             % (src.numel(), L.fp4_calib_mfma_src_bytes(grid)))
     out = torch.empty(grid * 256, dtype=torch.float32, device=device)
     clocks = torch.zeros((launches, grid * 4, 2), dtype=torch.int64, device=device)
     stream = torch.cuda.current_stream(device)
@@ -68,9 +96,9 @@ def mfma_ceiling(device, iters: int = 20000, warmup: int = 20, launches: int = 1
     tflops = L.fp4_calib_mfma_flops(grid, iters) / sec / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "sclk_GHz": sclk / 1e9, "grid": grid, "iters": iters,
             "ms_per_launch": sec * 1e3,
-            "what": "scaled FP4 MFMA 32x32x64 only, random E2M1 operands in registers, the Wgrad "
+            "what": "scaled FP4 MFMA 32x32x64 only, %s E2M1 operands in registers, the Wgrad "
                     "GEMM's wave tile (7x2 accumulators, two fragment sets), one workgroup of 4 "
-                    "waves per CU"}
+                    "waves per CU" % ("random" if operands is None else "the product's own")}
 
 
 STAMPS = 32                  # workgroups per clock stamp (FP4_CALIB_STAMPS)

@@ -90,12 +90,20 @@ __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* l
 }
 
 // Scaled FP4 MFMA (32x32x64, both operands E2M1, fp32 accumulate) taking the
-// E8M0 scales from byte 0 or byte 2 of the scale registers.
-__device__ __forceinline__ v16f mfma_fp4_byte0(v8i b, v8i a, v16f c, uint32_t sb, uint32_t sa) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 0, (int)sb, 0, (int)sa);
+// E8M0 scales from byte S of the scale registers.
+template <int S>
+__device__ __forceinline__ v16f mfma_fp4(v8i b, v8i a, v16f c, uint32_t sb, uint32_t sa) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, S, (int)sb, S, (int)sa);
 }
-__device__ __forceinline__ v16f mfma_fp4_byte2(v8i b, v8i a, v16f c, uint32_t sb, uint32_t sa) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 4, 4, 2, (int)sb, 2, (int)sa);
+
+// The scale word a lane feeds the MFMAs of one 256-k stage: the stage's 8
+// block scales of its row are bytes 0..7 of (hi:lo); k-step s uses block
+// 2 s + (lane / 32), so lane half h keeps bytes h, 2 + h, 4 + h, 6 + h, and
+// k-step s reads byte s of the word -- one byte permute per stage instead of
+// a shift before every MFMA.  Formed when the stage starts: at load time it
+// would wait for loads issued stages ahead.
+__device__ __forceinline__ uint32_t stage_scale_word(uint32_t lo, uint32_t hi, int h) {
+    return __builtin_amdgcn_perm(hi, lo, h ? 0x07050301u : 0x06040200u);
 }
 
 // Maps the hardware block index to a (tile_m, tile_n) pair: XCD-contiguous
@@ -293,7 +301,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         if constexpr (KTAIL) off |= (!dead && s == nks - 1 && half_tail) ? kOob : 0u;
         return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, off, soff, 0));
     };
-    // B scales of stage kt: this lane's row of fragment j, 8 bytes.
+    // B scales of stage kt: this lane's row of fragment j, 8 bytes (blocks
+    // past the contraction's end already set to 2^0).
     struct BSc { uint32_t w[FN][2]; };
     auto load_bsc = [&](int kt) -> BSc {
         if constexpr (FAST) {
@@ -342,26 +351,49 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
             const uint2 v = *reinterpret_cast<const uint2*>(slot + kACodes + (i * 32 + l32) * 8);
             sc.w[i][0] = v.x;
             sc.w[i][1] = v.y;
-            if constexpr (KTAIL) {
-                sc.w[i][0] = mask_scale_word(sc.w[i][0], (int64_t)kt * 8, nb);
-                sc.w[i][1] = mask_scale_word(sc.w[i][1], (int64_t)kt * 8 + 4, nb);
-            }
         }
     };
     // MFMAs of k-step s (0..3) of a stage: A fragments set, B ring slot r.
-    auto mfmas = [&](int s, int set, int r, const ASc& sa, const BSc& sb, int kt) {
+    // The stage's scale words (stage_scale_word) from its raw A and B scales;
+    // blocks past the contraction's end take 2^0.
+    struct SWords { uint32_t a[FM], b[FN]; };
+    auto stage_words = [&](const ASc& sa, const BSc& sb, int kt) -> SWords {
+        SWords w;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            uint32_t lo = sa.w[i][0], hi = sa.w[i][1];
+            if constexpr (KTAIL) {
+                lo = mask_scale_word(lo, (int64_t)kt * 8, nb);
+                hi = mask_scale_word(hi, (int64_t)kt * 8 + 4, nb);
+            }
+            w.a[i] = stage_scale_word(lo, hi, h);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            uint32_t lo = sb.w[j][0], hi = sb.w[j][1];
+            if constexpr (KTAIL) {
+                lo = mask_scale_word(lo, (int64_t)kt * 8, nb);
+                hi = mask_scale_word(hi, (int64_t)kt * 8 + 4, nb);
+            }
+            w.b[j] = stage_scale_word(lo, hi, h);
+        }
+        return w;
+    };
+    auto mfmas = [&](int s, int set, int r, const SWords& sw) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const v8i af = __builtin_shufflevector(fa[set][i], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-            const uint32_t wa = sa.w[i][s >> 1] >> (8 * h);
+            const uint32_t wa = sw.a[i];
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const v8i bf = __builtin_shufflevector(fb[r][j], v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
-                uint32_t wbw = sb.w[j][s >> 1];
-                if constexpr (KTAIL) wbw = mask_scale_word(wbw, (int64_t)kt * 8 + 4 * (s >> 1), nb);
-                const uint32_t wb = wbw >> (8 * h);
-                acc[i][j] = (s & 1) ? mfma_fp4_byte2(bf, af, acc[i][j], wb, wa)
-                                    : mfma_fp4_byte0(bf, af, acc[i][j], wb, wa);
+                const uint32_t wb = sw.b[j];
+                switch (s) {
+                    case 0: acc[i][j] = mfma_fp4<0>(bf, af, acc[i][j], wb, wa); break;
+                    case 1: acc[i][j] = mfma_fp4<1>(bf, af, acc[i][j], wb, wa); break;
+                    case 2: acc[i][j] = mfma_fp4<2>(bf, af, acc[i][j], wb, wa); break;
+                    default: acc[i][j] = mfma_fp4<3>(bf, af, acc[i][j], wb, wa); break;
+                }
             }
         }
     };
@@ -377,13 +409,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         uint8_t* const cur = slots[u];
         uint8_t* const ahead = slots[(u + 3) % kSlots];
         uint8_t* const next = slots[(u + 1) % kSlots];
-        const ASc& sa = asc[u & 1];
         ASc& nsa = asc[(u + 1) & 1];
-        const BSc& sb = bsc[u];
+        const SWords sw = stage_words(asc[u & 1], bsc[u], kt);
 #pragma unroll
         for (int s = 0; s < kKS - 1; ++s) {
             read_afrags(cur, s + 1, (s + 1) & 1);
-            mfmas(s, s & 1, (4 * u + s) % kRing, sa, sb, kt);
+            mfmas(s, s & 1, (4 * u + s) % kRing, sw);
 #pragma unroll
             for (int j = 0; j < FN; ++j) fb[(4 * u + s) % kRing][j] = load_b(4 * kt + s + kRing, j);
             dma_a(kt + 3, ahead, kdma(s), kdma(s + 1), s == 0);
@@ -411,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         barrier_after_wait();
         read_ascales(next, kt + 1, nsa);
         read_afrags(next, 0, 0);
-        mfmas(kKS - 1, 1, (4 * u + 3) % kRing, sa, sb, kt);
+        mfmas(kKS - 1, 1, (4 * u + 3) % kRing, sw);
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[(4 * u + 3) % kRing][j] = load_b(4 * kt + 3 + kRing, j);
         constexpr int kM = FM * FN, kDs = 2 * FM;

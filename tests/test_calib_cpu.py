@@ -71,3 +71,22 @@ def test_stamp_count_matches_header():
     from fp4_precision_gemms_amd.calib import STAMPS
     m = re.search(r"#define FP4_CALIB_STAMPS (\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == STAMPS
+
+
+def test_operand_fragments_follow_the_loop_layout():
+    """Wave w's fragments f = set * 9 + i (A, i < 7) and set * 9 + 7 + j (B)
+    are the 1 KB pieces 14 w + 7 set + i of A and 4 w + 2 set + j of B."""
+    import torch
+    from fp4_precision_gemms_amd import calib
+    a = (torch.arange(40 * 1024) % 253).to(torch.uint8)        # 40 pieces
+    b = (torch.arange(6 * 1024) % 241).to(torch.uint8)         # 6 pieces
+    src = calib.operand_fragments(a, b, 5)
+    assert src.numel() == 5 * 18 * 1024 and src.is_contiguous()
+    f = src.reshape(5, 2, 9, 1024)
+    pa, pb = a.reshape(-1, 1024), b.reshape(-1, 1024)
+    for w in range(5):
+        for s in range(2):
+            for i in range(7):
+                assert torch.equal(f[w, s, i], pa[(14 * w + 7 * s + i) % 40])
+            for j in range(2):
+                assert torch.equal(f[w, s, 7 + j], pb[(4 * w + 2 * s + j) % 6])
