@@ -34,6 +34,10 @@
 //     k-step's two 1 KB fragments are one contiguous load each (the tiled
 //     layout), issued 8 k-steps ahead into a register ring; B scales come
 //     from HBM one stage group per load, two stages ahead.
+//   - Scales: when a stage starts, each lane turns its rows' 8 block scales
+//     of the stage into one word by a byte permute (the 4 blocks its lane
+//     half uses), and k-step s reads byte s of it through the MFMA's scale
+//     byte select -- no per-MFMA arithmetic on the operand path.
 //   - A contraction that is not a multiple of 256 (KTAIL) zero-fills chunks
 //     past the end through out-of-range buffer offsets and sets the scale
 //     bytes of blocks past the end to 127 (2^0).
