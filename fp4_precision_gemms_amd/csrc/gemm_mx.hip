@@ -344,15 +344,29 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     struct ASc { uint32_t w[FM][2]; };
     ASc asc[2];                    // A scales of the current and next stage
 
-    auto read_afrags = [&](const uint8_t* slot, int s, int set) {
+    // Per-slot lane bases of the LDS reads (this lane's 16 bytes of a
+    // fragment; its row's 8 scale bytes): the rest of each address then fits
+    // the LDS read's 16-bit immediate also in the slots past 64 KB, instead
+    // of costing an OR before every read.  The lane offsets pass through an
+    // empty asm statement so that the bases are not folded back into them.
+    uint32_t lo16 = (uint32_t)lane * 16, lo8 = (uint32_t)l32 * 8;
+    asm volatile("" : "+v"(lo16), "+v"(lo8));
+    const uint8_t* fbase[kSlots];
+    const uint8_t* sbase[kSlots];
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+        fbase[q] = slots[q] + lo16;
+        sbase[q] = slots[q] + kACodes + lo8;
+    }
+    auto read_afrags = [&](int q, int s, int set) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-            fa[set][i] = *reinterpret_cast<const v4i*>(slot + i * 4096 + s * 1024 + lane * 16);
+            fa[set][i] = *reinterpret_cast<const v4i*>(fbase[q] + i * 4096 + s * 1024);
     };
-    auto read_ascales = [&](const uint8_t* slot, int kt, ASc& sc) {
+    auto read_ascales = [&](int q, int kt, ASc& sc) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const uint2 v = *reinterpret_cast<const uint2*>(slot + kACodes + (i * 32 + l32) * 8);
+            const uint2 v = *reinterpret_cast<const uint2*>(sbase[q] + i * 32 * 8);
             sc.w[i][0] = v.x;
             sc.w[i][1] = v.y;
         }
@@ -410,14 +424,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     // registers).  Stage kt + 3 is loaded into slot (u + 3) mod 4, B scales
     // of stage kt + 2 into the B scale ring, B k-steps 8 ahead into the B ring.
     auto run_stage = [&](int u, int kt) {
-        uint8_t* const cur = slots[u];
         uint8_t* const ahead = slots[(u + 3) % kSlots];
-        uint8_t* const next = slots[(u + 1) % kSlots];
         ASc& nsa = asc[(u + 1) & 1];
         const SWords sw = stage_words(asc[u & 1], bsc[u], kt);
 #pragma unroll
         for (int s = 0; s < kKS - 1; ++s) {
-            read_afrags(cur, s + 1, (s + 1) & 1);
+            read_afrags(u, s + 1, (s + 1) & 1);
             mfmas(s, s & 1, (4 * u + s) % kRing, sw);
 #pragma unroll
             for (int j = 0; j < FN; ++j) fb[(4 * u + s) % kRing][j] = load_b(4 * kt + s + kRing, j);
@@ -444,8 +456,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
         // prologue's order gives exactly that count for the first stages).
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kWaitStage));
         barrier_after_wait();
-        read_ascales(next, kt + 1, nsa);
-        read_afrags(next, 0, 0);
+        read_ascales((u + 1) % kSlots, kt + 1, nsa);
+        read_afrags((u + 1) % kSlots, 0, 0);
         mfmas(kKS - 1, 1, (4 * u + 3) % kRing, sw);
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[(4 * u + 3) % kRing][j] = load_b(4 * kt + 3 + kRing, j);
@@ -520,8 +532,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        read_ascales(slots[0], kfirst, asc[0]);
-        read_afrags(slots[0], 0, 0);
+        read_ascales(0, kfirst, asc[0]);
+        read_afrags(0, 0, 0);
         for (int kt = kfirst; kt < nk; kt += kSlots) {
             run_stage(0, kt);
             run_stage(1, kt + 1);
