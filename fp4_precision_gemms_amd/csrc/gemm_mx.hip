@@ -507,8 +507,19 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int kEpiStores = FM * 8;
 
     bool early = false;   // this tile's prologue was issued during the previous epilogue
+    if constexpr (FAST) {
+        // Every tile is full: the first tile's prologue goes out here and
+        // every later one during the previous tile's epilogue, so the loop
+        // below has a single prologue site (with two, the compiler moved the
+        // prologue's B fragments between registers in the middle of the
+        // epilogue, waiting for them there).
+        set_tile(blockIdx.x);
+        prologue();
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        early = true;
+    }
     for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        if (!early) {
+        if (!FAST && !early) {
             if (t != (int)blockIdx.x) {
                 // every wave is done with the previous tile's LDS before it is refilled
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
