@@ -23,12 +23,14 @@ with no host synchronization in between (the card must not idle before the
 measured windows): back-to-back steps for --settle-ms of GPU time whatever W
 is (reported as "settle"), the K timed steps between two events holding
 nothing but their launches, with a clock-stamp kernel on either side
-(timed_clock), and the event pass.  Prints one JSON line.
+(timed_clock), and the per-kernel windows: K launches of each kernel back
+to back between two events.  Prints one JSON line.
 `value` is Wgrad TFLOP/s including quantization (2 T N K flops per step);
-the roofline object describes the dominant kernel (the GEMM) from HIP
-events around each launch over a second pass of K steps; breakdown holds
-both kernels, the quantizer's launches alone (K back to back, after 50 ms of
-them) and the card's device-to-device copy rate; --flush adds a pass
+the roofline object describes the dominant kernel (the GEMM) from its
+window (an event record between two launches opens a gap of about 5 us
+before the second, so events around every launch would count that gap as
+the kernel's); breakdown holds both kernels' windows, what the timed step
+spends beyond them, and the card's device-to-device copy rate; --flush adds a pass
 with a 1 GiB write before each step (cold L2 and memory-side cache, median
 and minimum); cpu_baseline times the plain CPU oracle on a bounded sample of
 the same workload and checks the last timed step's outputs against it
@@ -359,7 +361,8 @@ def layer_bench(args) -> int:
     cols: along the second axis, no rotation), then Fprop Y = X W^T, Dgrad
     dX = dY W and Wgrad dW = dY^T X through the role entry points (fp32
     outputs).  One JSON line: 3 * 2 T N K flops over the step, and each
-    launch's average time from HIP events around it."""
+    launch's average time over K launches of it back to back between two
+    HIP events."""
     import numpy as np
     import torch
 
@@ -396,21 +399,20 @@ def layer_bench(args) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    # per-launch times, in a second pass with events around each launch,
-    # right behind the timed steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in launches] for _ in range(args.steps)]
+    # per-launch times: each launch K times back to back between two events,
+    # right behind the timed steps (events around every launch would count
+    # the gap an event record opens before the next launch)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in launches]
 
-    def event_pass():
-        for i in range(args.steps):
-            for (a, b), (_, fn) in zip(ev[i], launches):
-                a.record()
+    def windows():
+        for (a, b), (_, fn) in zip(ev, launches):
+            a.record()
+            for _ in range(args.steps):
                 fn()
-                b.record()
+            b.record()
 
-    ms, settle_steps, settle_ms = gapless_window(torch, dev, step, args.steps, args.settle_ms, event_pass)
-    per = {name: 1e3 * sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)) / args.steps
-           for j, (name, _) in enumerate(launches)}
+    ms, settle_steps, settle_ms = gapless_window(torch, dev, step, args.steps, args.settle_ms, windows)
+    per = {name: 1e3 * ev[j][0].elapsed_time(ev[j][1]) / args.steps for j, (name, _) in enumerate(launches)}
     flop = 2.0 * T * N * K
     qbytes = {"quant_X_dual": T * K * (2 + 1 + 1 / 16), "quant_W_dual": N * K * (2 + 1 + 1 / 16),
               "quant_dY_dual": T * N * (2 + 1 + 1 / 16)}
@@ -435,6 +437,7 @@ def layer_bench(args) -> int:
                      "unit": "TFLOP/s", "frac": flop / (gemm_us * 1e-6) / 1e12 / MXFP4_PEAK_TFLOPS,
                      "traffic": None},
         "settle": {"steps": settle_steps, "ms": settle_ms},
+        "step_minus_launches_us": ms * 1e3 - sum(per.values()),
         "breakdown": breakdown}), flush=True)
     return 0
 
@@ -601,7 +604,14 @@ def main() -> int:
     snap = None
     if not args.no_cpu_baseline:
         snap = [torch.empty_like(t) for t in (dytq, dyts, xtq, xts, dw)]
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # each kernel's window: its launch K times back to back (the quantizer
+    # with the first step's seeds, the GEMM on the last step's operands)
+    _, q_sign, _, (q_sr_dy, q_sr_x) = step_settings(args.variant, 0)
+    kernels = [("quant", lambda: F.fp4_wgrad_quantize(dY, X, 32, had, q_sign, rnd, q_sr_dy, q_sr_x,
+                                                      out=(dytq, dyts, xtq, xts))),
+               ("gemm", lambda: F.fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=dw))]
+    win = {name: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for name, _ in kernels}
     s0 = torch.cuda.Event(enable_timing=True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0.record(stream)
@@ -621,10 +631,13 @@ def main() -> int:
     if snap is not None:
         for d, t in zip(snap, (dytq, dyts, xtq, xts, dw)):
             d.copy_(t)
-    # per-launch durations: the same number of steps again, HIP events on the
-    # launch stream around each launch
-    for i in range(args.steps):
-        step(events[i])
+    # per-kernel launch durations: K launches of each back to back between
+    # two events on the launch stream, still without a host synchronization
+    for name, fn in kernels:
+        win[name][0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        win[name][1].record(stream)
     torch.cuda.synchronize(dev)
     settle_ms = s0.elapsed_time(start)
     ms_step = start.elapsed_time(stop) / args.steps
@@ -634,26 +647,12 @@ def main() -> int:
         timed = (last_timed, *(t.cpu().numpy() for t in snap))
         del snap
 
-    def avg(a, b):
-        return sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
-
-    t_q, t_gemm = avg(0, 1), avg(1, 2)
+    t_q, t_gemm = (win[name][0].elapsed_time(win[name][1]) / args.steps for name, _ in kernels)
     flops = 2.0 * T * N * K
     gemm_tflops = flops / (t_gemm * 1e-3) / 1e12
     q_bytes = quant_bytes(T * N) + quant_bytes(T * K)
     q_gbs = q_bytes / (t_q * 1e-3) / 1e9
 
-    # the quantizer alone: the same launch back to back, no GEMM between
-    # (against its time inside the step, where it follows the GEMM)
-    _, q_sign, _, (q_sr_dy, q_sr_x) = step_settings(args.variant, 0)
-
-    def qstep():
-        F.fp4_wgrad_quantize(dY, X, 32, had, q_sign, rnd, q_sr_dy, q_sr_x, out=(dytq, dyts, xtq, xts))
-
-    for _ in range(10):
-        qstep()
-    t_q_alone = gapless_window(torch, dev, qstep, args.steps, 50.0)[0]
-    q_alone_gbs = q_bytes / (t_q_alone * 1e-3) / 1e9
     # the box's device-to-device copy rate (512 MiB each way), the practical
     # ceiling of a read-once write-once kernel
     csrc = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -711,7 +710,8 @@ def main() -> int:
                      "frac": gemm_tflops / MXFP4_PEAK_TFLOPS, "traffic": traffic},
         "settle": {"steps": settle_steps, "ms": settle_ms,
                    "what": "back-to-back steps right before the timed ones (GPU time), whatever --warmup is; "
-                           "settle, timed steps and event pass run with no host synchronization between them"},
+                           "settle, timed steps and the per-kernel windows run with no host synchronization "
+                           "between them"},
         "timed_clock": {"sclk_GHz": sclk,
                         "what": "shader clock counter (s_memtime) against the 100 MHz reference "
                                 "(s_memrealtime) between clock-stamp launches on either side of the "
@@ -719,9 +719,11 @@ def main() -> int:
                                 "cores' rate is not proportional to it (measured: equal kernel times "
                                 "at rates 13 % apart)"},
         "breakdown": {"quant_dY_X_ms": t_q, "gemm_ms": t_gemm,
+                      "step_minus_kernels_ms": ms_step - t_q - t_gemm,
+                      "what": "each kernel's average launch time over K launches of it back to back "
+                              "between two events on the launch stream, right after the timed steps; "
+                              "step_minus_kernels: what a timed step takes beyond the two",
                       "quantizer_GBps": q_gbs, "quantizer_frac_hbm": q_gbs / HBM_PEAK_GBS,
-                      "quantizer_alone_ms": t_q_alone, "quantizer_alone_GBps": q_alone_gbs,
-                      "quantizer_alone_frac_hbm": q_alone_gbs / HBM_PEAK_GBS,
                       "d2d_copy_GBps": copy_gbs, "quantizer_frac_copy": q_gbs / copy_gbs,
                       "gemm_TFLOPs": gemm_tflops,
                       "gemm_frac_of_peak_at_timed_sclk": gemm_tflops / (MXFP4_PEAK_TFLOPS * sclk / 2.4)},
