@@ -30,9 +30,9 @@ the roofline object describes the dominant kernel (the GEMM) from its
 window (an event record between two launches opens a gap of about 5 us
 before the second, so events around every launch would count that gap as
 the kernel's); breakdown holds both kernels' windows, what the timed step
-spends beyond them, and the card's device-to-device copy rate; --flush adds a pass
-with a 1 GiB write before each step (cold L2 and memory-side cache, median
-and minimum); cpu_baseline times the plain CPU oracle on a bounded sample of
+spends beyond them, and the card's device-to-device copy rate; --flush adds
+passes with a 1 GiB write before each step, then before each kernel alone
+(cold L2 and memory-side cache; median and minimum); cpu_baseline times the plain CPU oracle on a bounded sample of
 the same workload and checks the last timed step's outputs against it
 (timed_run_parity); mfma_ceiling is the scaled FP4 MFMA rate the card
 sustains on random operands with no memory traffic at all
@@ -568,19 +568,13 @@ def main() -> int:
     rnd = F.SR if rnd_name.startswith("sr") else F.RTN
     counter = [0]
 
-    def step(ev=None):
+    def step():
         # both Wgrad operands (one rotation, one launch), then the GEMM
         i = counter[0]
         counter[0] += 1
         _, sign_seed, _, (sr_dy, sr_x) = step_settings(args.variant, i)
-        if ev is not None:
-            ev[0].record(stream)
         F.fp4_wgrad_quantize(dY, X, 32, had, sign_seed, rnd, sr_dy, sr_x, out=(dytq, dyts, xtq, xts))
-        if ev is not None:
-            ev[1].record(stream)
         F.fp4_gemm_wgrad(dytq, dyts, xtq, xts, out=dw)
-        if ev is not None:
-            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -669,24 +663,32 @@ def main() -> int:
     del csrc, cdst
     flushed = None
     if args.flush:
-        # each step after a 1 GiB write (evicts L2 and the 256 MB
-        # memory-side cache), events around the step only
+        # each measured call after a 1 GiB write (evicts L2 and the 256 MB
+        # memory-side cache), HIP events at its two ends only: the whole
+        # step, then each kernel in a loop of its own
         fbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        times = []
-        for _ in range(args.steps):
-            fbuf.zero_()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(e)
-            torch.cuda.synchronize(dev)
-            times.append((e[0].elapsed_time(e[2]), e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])))
-        del fbuf
         import statistics
-        flushed = {"steps": len(times), "flush_bytes": 1 << 30,
-                   "step_ms_median": statistics.median(t[0] for t in times),
-                   "step_ms_min": min(t[0] for t in times),
-                   "quant_ms_median": statistics.median(t[1] for t in times),
-                   "gemm_ms_median": statistics.median(t[2] for t in times),
-                   "gemm_ms_min": min(t[2] for t in times)}
+
+        def cold(fn):
+            times = []
+            for _ in range(args.steps):
+                fbuf.zero_()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize(dev)
+                times.append(e0.elapsed_time(e1))
+            return statistics.median(times), min(times)
+
+        st_med, st_min = cold(step)
+        q_med, q_min = cold(kernels[0][1])
+        g_med, g_min = cold(kernels[1][1])
+        del fbuf
+        flushed = {"steps": args.steps, "flush_bytes": 1 << 30,
+                   "step_ms_median": st_med, "step_ms_min": st_min,
+                   "quant_ms_median": q_med, "quant_ms_min": q_min,
+                   "gemm_ms_median": g_med, "gemm_ms_min": g_min}
     traffic = traffic_per_launch(w.name)
     out = {
         "metric": METRIC if (w.name, args.variant) == ("gate_up", "det-rtn") else
