@@ -582,7 +582,7 @@ def main() -> int:
     # settle: back-to-back steps for a fixed stretch of GPU time, whatever
     # --warmup is (the first tens of milliseconds of load run at other
     # clocks).  The step count comes from a short probe; the settle steps,
-    # the timed steps and the event pass are then enqueued with no host
+    # the timed steps and the per-kernel windows are then enqueued with no host
     # synchronization between them, so the card never idles before or
     # between the measured windows (after even a short idle the next few
     # milliseconds run slower, which a 20-step window would measure).
