@@ -509,17 +509,19 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     bool early = false;   // this tile's prologue was issued during the previous epilogue
     if constexpr (FAST) {
         // Every tile is full: the first tile's prologue goes out here and
-        // every later one during the previous tile's epilogue, so the loop
-        // below has a single prologue site (with two, the compiler moved the
-        // prologue's B fragments between registers in the middle of the
-        // epilogue, waiting for them there).
+        // every later one during the previous tile's epilogue (accumulation
+        // aside), so the loop below has a single prologue site (with two, the
+        // compiler moved the prologue's B fragments between registers in the
+        // middle of the epilogue, waiting for them there).
         set_tile(blockIdx.x);
         prologue();
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
         early = true;
     }
     for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        if (!FAST && !early) {
+        // (an accumulating fast-path launch issues no prologue during its
+        // epilogues, which read C: its later tiles take theirs here)
+        if ((!FAST || ACC) && !early) {
             if (t != (int)blockIdx.x) {
                 // every wave is done with the previous tile's LDS before it is refilled
                 __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));

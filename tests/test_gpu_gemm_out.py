@@ -116,11 +116,15 @@ def test_role_entry_points_equal_gemm_mx():
 # output mode.  (14336, 4096): 1024 full 224 x 256 tiles; (14300, 4000):
 # ragged last tile row and column; (4096, 14336): 256 x 224 tiles;
 # (8192, 8192): 256 x 256 tiles.
-MULTI_TILE = [(14336, 4096, 512), (14300, 4000, 512), (4096, 14336, 512), (8192, 8192, 512)]
+# With K a multiple of 1024 and full tiles the launches take the fast path:
+# (14336, 4096, 1024) its 224 x 256 kernel, (8192, 8192, 1024) its 256 x 256
+# one, in every output mode, accumulation into fp32 and bf16 included.
+MULTI_TILE = [(14336, 4096, 512), (14300, 4000, 512), (4096, 14336, 512), (8192, 8192, 512),
+              (14336, 4096, 1024), (8192, 8192, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", MULTI_TILE)
-@pytest.mark.parametrize("mode", ["f32", "bf16", "f32_acc"])
+@pytest.mark.parametrize("mode", ["f32", "bf16", "f32_acc", "bf16_acc"])
 def test_multi_tile_sampled(M, N, K, mode):
     rng, aq, as_, bq, bs = operands(M, N, K, M + 3 * N + K)
     say("gemm_mx multi-tile", mode, M, N, K)
@@ -131,8 +135,11 @@ def test_multi_tile_sampled(M, N, K, mode):
         out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     else:
         c_old = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).cuda()
+        if mode == "bf16_acc":
+            c_old = c_old.to(torch.bfloat16)
         out = c_old.clone()
-    got = run(aq, as_, bq, bs, out, F.OUT_BF16 if mode == "bf16" else F.OUT_F32, mode == "f32_acc")
+    got = run(aq, as_, bq, bs, out, F.OUT_BF16 if mode.startswith("bf16") else F.OUT_F32,
+              mode.endswith("_acc"))
     # whole rows and columns at tile edges and in the middle, then random
     rows = [0, 223, 224, 255, 256, M // 2 + 17, M - 1]
     cols = [0, 223, 224, 255, 256, N // 2 + 5, N - 1]
@@ -145,6 +152,9 @@ def test_multi_tile_sampled(M, N, K, mode):
     elif mode == "f32":
         gemm_check(g, ref, mag, TOL)
     else:
-        old = c_old.cpu().numpy()[mi, ni].astype(np.float64)
-        gemm_check(g, ref + old, mag + np.abs(old), TOL)
+        old = c_old.float().cpu().numpy()[mi, ni].astype(np.float64)
+        if mode == "bf16_acc":
+            bf16_check(g, ref + old, mag + np.abs(old))
+        else:
+            gemm_check(g, ref + old, mag + np.abs(old), TOL)
     assert np.isfinite(got).all()
