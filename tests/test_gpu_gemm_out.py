@@ -119,8 +119,10 @@ def test_role_entry_points_equal_gemm_mx():
 # With K a multiple of 1024 and full tiles the launches take the fast path:
 # (14336, 4096, 1024) its 224 x 256 kernel, (8192, 8192, 1024) its 256 x 256
 # one, in every output mode, accumulation into fp32 and bf16 included.
+# (14300, 4000, 800): a contraction that is no multiple of 256 (25 blocks:
+# a partial last stage and a half k-step) with ragged tiles.
 MULTI_TILE = [(14336, 4096, 512), (14300, 4000, 512), (4096, 14336, 512), (8192, 8192, 512),
-              (14336, 4096, 1024), (8192, 8192, 1024)]
+              (14336, 4096, 1024), (8192, 8192, 1024), (14300, 4000, 800)]
 
 
 @pytest.mark.parametrize("M,N,K", MULTI_TILE)
