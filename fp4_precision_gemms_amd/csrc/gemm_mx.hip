@@ -507,6 +507,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_tn(
     constexpr int kEpiStores = FM * 8;
 
     bool early = false;   // this tile's prologue was issued during the previous epilogue
+    // Staggered start: workgroup b begins b x 64 cycles late (about 8 us for
+    // 256 workgroups), so that their tile boundaries -- an epilogue writing
+    // the finished tile while the next tile's first stages load -- do not
+    // all fall at the same moment: measured 1.6-2.4 % faster on launches of
+    // several rounds.  A single round would only pay the delay.
+    if (ntiles > (int)gridDim.x) {
+        for (int q = 0; q < (int)blockIdx.x; ++q) __builtin_amdgcn_s_sleep(1);
+    }
     if constexpr (FAST) {
         // Every tile is full: the first tile's prologue goes out here and
         // every later one during the previous tile's epilogue (accumulation
