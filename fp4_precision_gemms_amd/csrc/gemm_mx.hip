@@ -48,6 +48,8 @@
 //     LDS slot and stores whole rows per instruction.  When the tile and the
 //     workgroup's next tile are both full, the next tile's first stages are
 //     issued before the epilogue (into the other three slots).
+//   - Launches of several rounds start their workgroups staggered, so that
+//     the tile boundaries of the 256 workgroups do not coincide.
 #include "fp4_device.hpp"
 #include "fp4_launch.hpp"
 
